@@ -1,0 +1,185 @@
+"""Benchmark: causal attention forward and forward+backward on one MI355X.
+
+One step = the whole hot path over one batch of seeded synthetic inputs that
+are already resident in HBM: fa_fwd (O, L), fa_bwd_preprocess (D) and fa_bwd
+(dQ, dK, dV), all through the C ABI on one stream.  Throughput counts the
+algorithmic causal FLOPs, 4*D per allowed (query, key) pair for the forward
+and 14*D per pair for forward+backward (five contractions in the backward;
+recomputation, masked halves of diagonal tiles and head-dimension padding are
+not counted).
+
+Prints one JSON line.  `roofline` covers the forward kernel (one kernel per
+fa_fwd call, timed with HIP events on the stream it runs on);
+`roofline_bwd` covers the backward launch pair of fa_bwd.  `cpu_baseline`
+times the fp64 CPU oracle on a bounded slice of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from exact_attention_causal_amd import fa  # noqa: E402
+from exact_attention_causal_amd.inputs import WORKLOADS, workload_inputs  # noqa: E402
+
+METRIC = "causal attention fwd & fwd+bwd TFLOP/s (bf16) + % of MFMA peak, 1 GPU"
+PEAK_BF16 = 2516.6   # TFLOP/s, dense bf16 matrix cores (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_F32 = 157.3     # TFLOP/s, dense fp32 matrix cores
+DEFAULT_WORKLOAD = "bf16_b1h16_s65536_d128"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="sequence prefix the CPU oracle baseline runs on")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, do, tokens):
+    """fp64 oracle forward+backward on the first `tokens` positions of every head.
+
+    Causal attention restricted to a prefix of the sequence is the same
+    computation on a smaller triangle, so its FLOP rate is the oracle's rate
+    on this workload's shapes and head dimension.
+    """
+    import oracle
+    S = min(tokens, w.S)
+    sl = [x[:, :, :S].double().numpy() for x in (q, k, v, do)]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    t0 = time.perf_counter()
+    oracle.backward(*sl, scale=w.scale, causal=True, nthreads=threads)
+    dt = time.perf_counter() - t0
+    pairs = w.B * w.H * S * (S + 1) // 2
+    return {"value": 14 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": dt,
+            "sample": f"fp64 oracle fwd+bwd on the first {S} tokens of all {w.B * w.H} heads "
+                      f"(causal prefix of the same Q/K/V/dO), 14*D*pairs FLOPs / wall time"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the heads shard across GPUs with no communication, see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    fa.load_library()
+    code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+    B, H, S, D = w.shape
+
+    log(f"generating inputs for {w.name}")
+    q, k, v, do = workload_inputs(w)
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, S), device=dev, dtype=torch.float32)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws_bytes = fa.fa_bwd_workspace_size(B, H, S, D, code)
+    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {fa.fa_strerror(rc)}")
+
+    def fwd():
+        check(fa.fa_fwd(qd, kd, vd, o, lse, B, H, S, D, w.scale, 1, code, sh), "fa_fwd")
+
+    def pre():
+        check(fa.fa_bwd_preprocess(o, dod, delta, B, H, S, D, code, sh), "fa_bwd_preprocess")
+
+    def bwd():
+        check(fa.fa_bwd(qd, kd, vd, dod, lse, delta, dq, dk, dv, ws, ws_bytes, B, H, S, D,
+                        w.scale, 1, code, sh), "fa_bwd")
+
+    log("warmup")
+    for _ in range(args.warmup):
+        fwd(); pre(); bwd()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+
+    # timed region: K whole steps, with per-entry-point events on the same stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        pre()
+        ev[i][2].record(stream)
+        bwd()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    t_pre = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    t_bwd = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    ms_step = wall * 1e3 / args.steps
+
+    pairs = w.causal_pairs()
+    f_fwd = 4 * D * pairs
+    f_all = 14 * D * pairs
+    peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_F32
+    value = f_all / (ms_step * 1e-3) / 1e12
+    fwd_tf = f_fwd / (t_fwd * 1e-3) / 1e12
+    bwd_tf = 10 * D * pairs / (t_bwd * 1e-3) / 1e12
+    esize = 2 if w.dtype == "bf16" else 4
+    tensor = B * H * S * D * esize
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
+        "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": True,
+                   "scale": w.scale},
+        "frac_of_peak": round(value / peak, 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_frac_of_peak": round(fwd_tf / peak, 4),
+        "ms": {"fwd": round(t_fwd, 4), "bwd_preprocess": round(t_pre, 4), "bwd": round(t_bwd, 4)},
+        "roofline": {"kernel": "fwd_kernel (fa_fwd)", "bound": "mfma", "achieved": round(fwd_tf, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tf / peak, 4),
+                     "traffic": None,
+                     "algorithmic_per_launch": {"flop": f_fwd, "bytes": 4 * tensor + 4 * B * H * S}},
+        "roofline_bwd": {"kernel": "dkdv_kernel + dq_kernel (fa_bwd)", "bound": "mfma",
+                         "achieved": round(bwd_tf, 2), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(bwd_tf / peak, 4)},
+    }
+    log(f"gpu done: {ms_step:.3f} ms/step, {value:.1f} TFLOP/s fwd+bwd, {fwd_tf:.1f} TFLOP/s fwd")
+    if not args.no_cpu_baseline:
+        log("cpu oracle baseline")
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, do, args.cpu_tokens)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

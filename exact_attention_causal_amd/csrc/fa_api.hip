@@ -1,0 +1,100 @@
+// fa_api.hip -- the C ABI (include/fa.h): argument checks, then launches.
+//
+// Every check runs on the host before anything is enqueued, so an invalid call
+// returns its status synchronously and touches no device state.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point.
+int check_shape(int B, int H, int S, int D, int dtype) {
+    if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA_EINVAL;
+    const long long bh = (long long)B * H;
+    if (bh > 0x7fffffffLL) return FA_EINVAL;
+    // elements per tensor must fit comfortably in 63 bits
+    const long long per_head = (long long)S * D;
+    if (bh > (0x3fffffffffffffffLL / per_head)) return FA_EINVAL;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_EUNSUPPORTED;
+    if (!fa::head_dim_supported(D)) return FA_EUNSUPPORTED;
+    return FA_OK;
+}
+
+int check_scale(float scale) {
+    if (!isfinite(scale) || !(scale > 0.f)) return FA_EINVAL;
+    return FA_OK;
+}
+
+int map_launch(int rc) {
+    if (rc == 0) return FA_OK;
+    if (rc == -2) return FA_EUNSUPPORTED;
+    if (rc == -1) return FA_EINVAL;
+    return FA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S,
+           int D, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_EINVAL;
+    if (causal != 0 && causal != 1) return FA_EINVAL;
+    if (int rc = check_scale(scale)) return rc;
+    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_EALIGN;
+    return map_launch(fa::launch_fwd(dtype, q, k, v, o, lse, B * H, S, D, scale, causal, stream));
+}
+
+int fa_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int S, int D,
+                      fa_dtype dtype, hipStream_t stream) {
+    if (!o || !dout || !delta) return FA_EINVAL;
+    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
+    if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return FA_EALIGN;
+    return map_launch(fa::launch_delta(dtype, o, dout, delta, B * H, S, D, stream));
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype) {
+    (void)B;
+    (void)H;
+    (void)S;
+    (void)D;
+    (void)dtype;
+    return 0;
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+           const float *delta, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+           int B, int H, int S, int D, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+    if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv) return FA_EINVAL;
+    if (causal != 0 && causal != 1) return FA_EINVAL;
+    if (int rc = check_scale(scale)) return rc;
+    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
+    const void *ptrs[] = {q, k, v, dout, lse, delta, dq, dk, dv};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return FA_EALIGN;
+    if (workspace_bytes < fa_bwd_workspace_size(B, H, S, D, dtype)) return FA_EWORKSPACE;
+    (void)workspace;
+    return map_launch(
+        fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv, B * H, S, D, scale, causal, stream));
+}
+
+const char *fa_strerror(int status) {
+    switch (status) {
+    case FA_OK: return "success";
+    case FA_EINVAL: return "invalid argument (null pointer, non-positive size, causal not 0/1, bad scale or size overflow)";
+    case FA_EUNSUPPORTED: return "unsupported head dimension or dtype";
+    case FA_EALIGN: return "pointer not 16-byte aligned";
+    case FA_EWORKSPACE: return "workspace too small";
+    case FA_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

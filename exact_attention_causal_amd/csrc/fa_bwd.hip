@@ -1,0 +1,477 @@
+// fa_bwd.hip -- causal FlashAttention-2 backward pass for gfx950.
+//
+// Follows the CS336 Assignment 2 handout, section 4.2.3 (Algorithm 2) and
+// Eq. 13-19: the probabilities are recomputed from the saved logsumexp,
+// P_ij = exp(S_ij - L_i), with the per-query statistic
+// D_i = rowsum(O o dO) computed beforehand, and the work is split into
+//   * a key/value-outer pass: one workgroup per tile of 128 keys (32 per
+//     wave) accumulates dV = P^T dO and dK = dS^T Q * scale over the query
+//     tiles at or below the diagonal;
+//   * a query-outer pass: one workgroup per tile of queries accumulates
+//     dQ = dS K * scale over the key tiles at or before the diagonal.
+// P (and dS) are computed twice, once in each pass, so no partial sums ever
+// cross workgroups: no atomics, no workspace, bit-reproducible results (the
+// handout's argument for Algorithm 2).
+//
+// Register/LDS mapping (see fa_common.hpp): in the key-outer pass the scores
+// are formed as S = Q K^T so that each lane owns one key column; P and dS
+// then feed dV^T = dO^T P and dK^T = Q^T dS directly as B operands, with
+// Q^T and dO^T staged transposed in LDS.  In the query-outer pass the scores
+// are S^T = K Q^T (each lane owns one query), and dS^T feeds
+// dQ^T = K^T dS^T with K^T staged transposed in LDS.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// ---------------------------------------------------------------- delta ---
+// D_i = sum_d O_id dO_id (handout Algorithm 2, first step), fp32 accumulation.
+// A workgroup reduces 64 rows: each thread multiplies 16-byte chunks, partial
+// sums meet in LDS, and 64 threads add a row's chunks in order.
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const T *__restrict__ o, const T *__restrict__ dout,
+                                                    float *__restrict__ delta, long long rows) {
+    constexpr int VEC = 16 / sizeof(T), CPR = D / VEC, RB = 64;
+    __shared__ float part[RB][CPR + 1];
+    const int tid = threadIdx.x;
+    const long long r0 = (long long)blockIdx.x * RB;
+    for (int u = tid; u < RB * CPR; u += 256) {
+        const int rr = u / CPR, c = u % CPR;
+        const long long row = r0 + rr;
+        float acc = 0.f;
+        if (row < rows) {
+            const size_t off = (size_t)row * D + c * VEC;
+            if constexpr (sizeof(T) == 2) {
+                bf16x8 a = *reinterpret_cast<const bf16x8 *>(o + off);
+                bf16x8 b = *reinterpret_cast<const bf16x8 *>(dout + off);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc = fmaf((float)a[t], (float)b[t], acc);
+            } else {
+                f32x4 a = *reinterpret_cast<const f32x4 *>(o + off);
+                f32x4 b = *reinterpret_cast<const f32x4 *>(dout + off);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc = fmaf(a[t], b[t], acc);
+            }
+        }
+        part[rr][c] = acc;
+    }
+    __syncthreads();
+    if (tid < RB && r0 + tid < rows) {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) s += part[tid][c];
+        delta[r0 + tid] = s;
+    }
+}
+
+// --------------------------------------------------------- key-outer dK/dV ---
+
+template <typename T, int D_, int BQ2_>
+struct KvTile {
+    static constexpr int D = D_, BQ2 = BQ2_;
+    static constexpr int NW = 4, NT = NW * kWave;
+    static constexpr int BKV = NW * 32;               // keys per workgroup
+    static constexpr int NQ2 = BQ2 / 32;              // 32-query blocks per query tile
+    static constexpr int KPL = Mma<T>::KPL;
+    static constexpr int NSD = D / 2 / KPL;
+    static constexpr int DP = (D + 31) / 32 * 32;
+    static constexpr int ND = DP / 32;
+    static constexpr int NI = 16 / KPL;
+    static constexpr int PAD = 16 / sizeof(T);
+    static constexpr int LDR = D + PAD;               // row-major Q / dO tile stride
+    static constexpr int LDT = BQ2 + PAD;             // transposed Q^T / dO^T tile stride
+    static_assert(D % 16 == 0 && BQ2 % 32 == 0, "tile shape");
+};
+
+template <typename T, typename C>
+__global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                     const T *__restrict__ v, const T *__restrict__ dout,
+                                                     const float *__restrict__ lse,
+                                                     const float *__restrict__ delta, T *__restrict__ dk,
+                                                     T *__restrict__ dv, int BH, int S, float c,
+                                                     float scale, int causal) {
+    using M = Mma<T>;
+    using frag = typename M::frag;
+    constexpr int D = C::D, BQ2 = C::BQ2;
+    __shared__ __attribute__((aligned(16))) T sQ[BQ2 * C::LDR];
+    __shared__ __attribute__((aligned(16))) T sdO[BQ2 * C::LDR];
+    __shared__ __attribute__((aligned(16))) T sQt[C::DP * C::LDT];
+    __shared__ __attribute__((aligned(16))) T sdOt[C::DP * C::LDT];
+    __shared__ __attribute__((aligned(16))) float sL[BQ2];
+    __shared__ __attribute__((aligned(16))) float sDl[BQ2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int bid = blockIdx.x;
+    const int kt = bid / BH;  // ascending: the tiles with the most query tiles go first
+    const int bh = bid % BH;
+    const size_t hoff = (size_t)bh * S * D;
+    q += hoff;
+    k += hoff;
+    v += hoff;
+    dout += hoff;
+    dk += hoff;
+    dv += hoff;
+    lse += (size_t)bh * S;
+    delta += (size_t)bh * S;
+    const int k0 = kt * C::BKV;
+    const int kw0 = k0 + wave * 32;
+    const int key = kw0 + l32;  // this lane's key column
+
+    if constexpr (C::DP > D) {
+        zero_lds_rows<T, C::LDT, C::NT>(sQt, D, C::DP, tid);
+        zero_lds_rows<T, C::LDT, C::NT>(sdOt, D, C::DP, tid);
+    }
+
+    // K^T and V^T fragments (B operands): lane owns key `key`, d-run of half h.
+    frag kf[C::NSD], vf[C::NSD];
+    if (key < S) {
+        load_run<T, C::NSD>(kf, k + (size_t)key * D + h * (D / 2));
+        load_run<T, C::NSD>(vf, v + (size_t)key * D + h * (D / 2));
+    } else {
+        zero_run<T, C::NSD>(kf);
+        zero_run<T, C::NSD>(vf);
+    }
+
+    f32x16 dK[C::ND], dV[C::ND];
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db) {
+        dK[db] = f32x16{};
+        dV[db] = f32x16{};
+    }
+
+    const int nq2 = (S + BQ2 - 1) / BQ2;
+    const int i0 = causal ? k0 / BQ2 : 0;
+
+    TileIO<T, BQ2, D, C::NT> qio, dio;
+    float lreg = 0.f, dreg = 0.f;
+    auto prefetch = [&](int qt) {
+        qio.load(q, qt * BQ2, S, tid);
+        dio.load(dout, qt * BQ2, S, tid);
+        if (tid < BQ2) {
+            const int qi = qt * BQ2 + tid;
+            // rows past the end get L = +inf, so exp(S - L) = 0 there
+            lreg = qi < S ? lse[qi] * kLog2e : INFINITY;
+            dreg = qi < S ? delta[qi] : 0.f;
+        }
+    };
+    if (i0 < nq2) prefetch(i0);
+
+    for (int it = i0; it < nq2; ++it) {
+        const int q0 = it * BQ2;
+        qio.template store_rows<C::LDR>(sQ, tid);
+        qio.template store_cols<C::LDT>(sQt, tid);
+        dio.template store_rows<C::LDR>(sdO, tid);
+        dio.template store_cols<C::LDT>(sdOt, tid);
+        if (tid < BQ2) {
+            sL[tid] = lreg;
+            sDl[tid] = dreg;
+        }
+        __syncthreads();
+        if (it + 1 < nq2) prefetch(it + 1);
+
+        const bool active = kw0 < S && !(causal && q0 + BQ2 - 1 < kw0);
+        if (active) {
+            const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
+#pragma unroll
+            for (int qb = 0; qb < C::NQ2; ++qb) {
+                // S block: rows = queries q0 + 32*qb + idx_of(r, h), col = key.
+                f32x16 s = f32x16{}, dp = f32x16{};
+                {
+                    frag qa[C::NSD];
+                    load_run<T, C::NSD>(qa, sQ + (qb * 32 + sigma(l32)) * C::LDR + h * (D / 2));
+#pragma unroll
+                    for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], kf[st], s);
+                }
+                {
+                    frag da[C::NSD];
+                    load_run<T, C::NSD>(da, sdO + (qb * 32 + sigma(l32)) * C::LDR + h * (D / 2));
+#pragma unroll
+                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], vf[st], dp);
+                }
+                float lv[16], dl[16];
+#pragma unroll
+                for (int hr = 0; hr < 2; ++hr) {
+                    const int base = qb * 32 + 16 * hr + 8 * h;
+                    const f32x4 l0 = *reinterpret_cast<const f32x4 *>(sL + base);
+                    const f32x4 l1 = *reinterpret_cast<const f32x4 *>(sL + base + 4);
+                    const f32x4 d0 = *reinterpret_cast<const f32x4 *>(sDl + base);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(sDl + base + 4);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        lv[8 * hr + t] = l0[t];
+                        lv[8 * hr + 4 + t] = l1[t];
+                        dl[8 * hr + t] = d0[t];
+                        dl[8 * hr + 4 + t] = d1[t];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
+                    if (need_mask) {
+                        const int qi = q0 + qb * 32 + idx_of(r, h);
+                        if ((causal && key > qi) || qi >= S) p = 0.f;
+                    }
+                    s[r] = p;
+                    dp[r] = p * (dp[r] - dl[r]);  // Eq. 17
+                }
+                frag pf[C::NI], sf[C::NI];
+                to_bfrag<T>(pf, s);
+                to_bfrag<T>(sf, dp);
+#pragma unroll
+                for (int db = 0; db < C::ND; ++db) {
+                    const int arow = (db * 32 + sigma(l32)) * C::LDT + qb * 32;
+                    frag a[C::NI];
+                    load_kblock<T>(a, sdOt + arow, h);
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) dV[db] = M::run(a[i], pf[i], dV[db]);  // Eq. 15
+                    load_kblock<T>(a, sQt + arow, h);
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) dK[db] = M::run(a[i], sf[i], dK[db]);  // Eq. 19
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (key < S) {
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr) {
+                const int d0 = db * 32 + 16 * hr + 8 * h;
+                if (d0 < D) {
+                    store8<T>(dk + (size_t)key * D + d0, dK[db], 8 * hr, scale);
+                    store8<T>(dv + (size_t)key * D + d0, dV[db], 8 * hr, 1.f);
+                }
+            }
+    }
+}
+
+// -------------------------------------------------------- query-outer dQ ---
+
+template <typename T, int D_, int NQB_, int BK_>
+struct QTile {
+    static constexpr int D = D_, NQB = NQB_, BK = BK_;
+    static constexpr int NW = 4, NT = NW * kWave;
+    static constexpr int BQ = NW * NQB * 32;
+    static constexpr int KPL = Mma<T>::KPL;
+    static constexpr int NSD = D / 2 / KPL;
+    static constexpr int NKB = BK / 32;
+    static constexpr int DP = (D + 31) / 32 * 32;
+    static constexpr int ND = DP / 32;
+    static constexpr int NI = 16 / KPL;
+    static constexpr int PAD = 16 / sizeof(T);
+    static constexpr int LDR = D + PAD;               // row-major K / V tile stride
+    static constexpr int LDT = BK + PAD;              // transposed K^T tile stride
+    static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
+};
+
+template <typename T, typename C>
+__global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                   const T *__restrict__ v, const T *__restrict__ dout,
+                                                   const float *__restrict__ lse,
+                                                   const float *__restrict__ delta, T *__restrict__ dq,
+                                                   int BH, int S, float c, float scale, int causal,
+                                                   int nqt) {
+    using M = Mma<T>;
+    using frag = typename M::frag;
+    constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
+    __shared__ __attribute__((aligned(16))) T sK[BK * C::LDR];
+    __shared__ __attribute__((aligned(16))) T sV[BK * C::LDR];
+    __shared__ __attribute__((aligned(16))) T sKt[C::DP * C::LDT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int bid = blockIdx.x;
+    const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
+    const int bh = bid % BH;
+    const size_t hoff = (size_t)bh * S * D;
+    q += hoff;
+    k += hoff;
+    v += hoff;
+    dout += hoff;
+    dq += hoff;
+    lse += (size_t)bh * S;
+    delta += (size_t)bh * S;
+    const int q0 = qt * C::BQ;
+    const int qw0 = q0 + wave * NQB * 32;
+
+    if constexpr (C::DP > D) zero_lds_rows<T, C::LDT, C::NT>(sKt, D, C::DP, tid);
+
+    // Q^T, dO^T fragments (B operands) and the row statistics of this lane's query.
+    frag qf[NQB][C::NSD], df[NQB][C::NSD];
+    float lq[NQB], dl[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = qw0 + qb * 32 + l32;
+        if (qi < S) {
+            load_run<T, C::NSD>(qf[qb], q + (size_t)qi * D + h * (D / 2));
+            load_run<T, C::NSD>(df[qb], dout + (size_t)qi * D + h * (D / 2));
+            lq[qb] = lse[qi] * kLog2e;
+            dl[qb] = delta[qi];
+        } else {
+            zero_run<T, C::NSD>(qf[qb]);
+            zero_run<T, C::NSD>(df[qb]);
+            lq[qb] = 0.f;
+            dl[qb] = 0.f;
+        }
+    }
+
+    f32x16 acc[NQB][C::ND];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db) acc[qb][db] = f32x16{};
+
+    const int qend = min(q0 + C::BQ, S);
+    int nkt = (S + BK - 1) / BK;
+    if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
+
+    TileIO<T, BK, D, C::NT> kio, vio;
+    kio.load(k, 0, S, tid);
+    vio.load(v, 0, S, tid);
+
+    for (int j = 0; j < nkt; ++j) {
+        const int j0 = j * BK;
+        kio.template store_rows<C::LDR>(sK, tid);
+        kio.template store_cols<C::LDT>(sKt, tid);
+        vio.template store_rows<C::LDR>(sV, tid);
+        __syncthreads();
+        if (j + 1 < nkt) {
+            kio.load(k, j0 + BK, S, tid);
+            vio.load(v, j0 + BK, S, tid);
+        }
+        const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
+        if (active) {
+            const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                frag ka[C::NSD], va[C::NSD];
+                load_run<T, C::NSD>(ka, sK + (kb * 32 + sigma(l32)) * C::LDR + h * (D / 2));
+                load_run<T, C::NSD>(va, sV + (kb * 32 + sigma(l32)) * C::LDR + h * (D / 2));
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    // S^T block: rows = keys j0 + 32*kb + idx_of(r, h), col = query.
+                    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+                    for (int st = 0; st < C::NSD; ++st) s = M::run(ka[st], qf[qb][st], s);
+#pragma unroll
+                    for (int st = 0; st < C::NSD; ++st) dp = M::run(va[st], df[qb][st], dp);
+                    const int qi = qw0 + qb * 32 + l32;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p = fast_exp2(fmaf(s[r], c, -lq[qb]));  // Eq. 14
+                        if (need_mask) {
+                            const int kk = j0 + kb * 32 + idx_of(r, h);
+                            if ((causal && kk > qi) || kk >= S) p = 0.f;
+                        }
+                        dp[r] = p * (dp[r] - dl[qb]);  // Eq. 17
+                    }
+                    frag sf[C::NI];
+                    to_bfrag<T>(sf, dp);
+#pragma unroll
+                    for (int db = 0; db < C::ND; ++db) {
+                        frag a[C::NI];
+                        load_kblock<T>(a, sKt + (db * 32 + sigma(l32)) * C::LDT + kb * 32, h);
+#pragma unroll
+                        for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(a[i], sf[i], acc[qb][db]);  // Eq. 18
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = qw0 + qb * 32 + l32;
+        if (qi < S) {
+#pragma unroll
+            for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+                for (int hr = 0; hr < 2; ++hr) {
+                    const int d0 = db * 32 + 16 * hr + 8 * h;
+                    if (d0 < D) store8<T>(dq + (size_t)qi * D + d0, acc[qb][db], 8 * hr, scale);
+                }
+        }
+    }
+}
+
+// ------------------------------------------------------------- launches ---
+
+template <typename T, int D>
+static int delta_for(const void *o, const void *dout, float *delta, int BH, int S, hipStream_t stream) {
+    const long long rows = (long long)BH * S;
+    const long long grid = (rows + 63) / 64;
+    if (grid > 0x7fffffffLL) return -1;
+    hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, (const T *)o,
+                       (const T *)dout, delta, rows);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+template <typename T, int D>
+static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+                   const float *delta, void *dq, void *dk, void *dv, int BH, int S, float scale,
+                   int causal, hipStream_t stream) {
+    // fp32 tiles are twice the bytes: halve the query tile of the key-outer pass for wide heads
+    using KC = KvTile<T, D, (sizeof(T) == 4 && D > 64) ? 32 : 64>;
+    using QC = QTile<T, D, 1, 64>;
+    const float c = scale * kLog2e;
+    const long long g1 = (long long)((S + KC::BKV - 1) / KC::BKV) * BH;
+    const int nqt = (S + QC::BQ - 1) / QC::BQ;
+    const long long g2 = (long long)nqt * BH;
+    if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
+    hipLaunchKernelGGL((dkdv_kernel<T, KC>), dim3((unsigned)g1), dim3(KC::NT), 0, stream, (const T *)q,
+                       (const T *)k, (const T *)v, (const T *)dout, lse, delta, (T *)dk, (T *)dv, BH, S,
+                       c, scale, causal);
+    if (hipGetLastError() != hipSuccess) return -5;
+    hipLaunchKernelGGL((dq_kernel<T, QC>), dim3((unsigned)g2), dim3(QC::NT), 0, stream, (const T *)q,
+                       (const T *)k, (const T *)v, (const T *)dout, lse, delta, (T *)dq, BH, S, c,
+                       scale, causal, nqt);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+#define FA_D_SWITCH(D, CALL)              \
+    switch (D) {                          \
+    case 16: { constexpr int DD = 16; return CALL; }   \
+    case 32: { constexpr int DD = 32; return CALL; }   \
+    case 64: { constexpr int DD = 64; return CALL; }   \
+    case 80: { constexpr int DD = 80; return CALL; }   \
+    case 96: { constexpr int DD = 96; return CALL; }   \
+    case 128: { constexpr int DD = 128; return CALL; } \
+    default: return -2;                   \
+    }
+
+template <typename T>
+static int delta_dispatch(int D, const void *o, const void *dout, float *delta, int BH, int S,
+                          hipStream_t stream) {
+    FA_D_SWITCH(D, (delta_for<T, DD>(o, dout, delta, BH, S, stream)))
+}
+
+template <typename T>
+static int bwd_dispatch(int D, const void *q, const void *k, const void *v, const void *dout,
+                        const float *lse, const float *delta, void *dq, void *dk, void *dv, int BH,
+                        int S, float scale, int causal, hipStream_t stream) {
+    FA_D_SWITCH(D, (bwd_for<T, DD>(q, k, v, dout, lse, delta, dq, dk, dv, BH, S, scale, causal, stream)))
+}
+
+int launch_delta(int dtype, const void *o, const void *dout, float *delta, int BH, int S, int D,
+                 hipStream_t stream) {
+    if (dtype == 1) return delta_dispatch<bf16>(D, o, dout, delta, BH, S, stream);
+    if (dtype == 0) return delta_dispatch<float>(D, o, dout, delta, BH, S, stream);
+    return -2;
+}
+
+int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
+               const float *lse, const float *delta, void *dq, void *dk, void *dv, int BH, int S,
+               int D, float scale, int causal, hipStream_t stream) {
+    if (dtype == 1)
+        return bwd_dispatch<bf16>(D, q, k, v, dout, lse, delta, dq, dk, dv, BH, S, scale, causal, stream);
+    if (dtype == 0)
+        return bwd_dispatch<float>(D, q, k, v, dout, lse, delta, dq, dk, dv, BH, S, scale, causal, stream);
+    return -2;
+}
+
+}  // namespace fa

@@ -1,0 +1,249 @@
+// fa_fwd.hip -- causal FlashAttention-2 forward pass for gfx950.
+//
+// Follows the CS336 Assignment 2 handout, section 4.2.2 (Algorithm 1): one
+// workgroup owns a tile of BQ queries of one head, keeps Q in registers and
+// streams key/value tiles of BK rows through LDS; the running row maximum m,
+// the running denominator l and the output accumulator are updated online
+// (the handout's m^(j), l^(j), O^(j) recurrences), and the epilogue writes
+// O = O^(Tk) / l and L = m + log l.  Key tiles that lie wholly above the
+// diagonal are not visited; only tiles that cross the diagonal or the end of
+// the sequence are masked (the handout's "Improve FlashAttention" ideas in
+// its leaderboard problem; lecture notes "A2 系统", section on online softmax:
+// skip fully masked blocks).
+//
+// gfx950 specifics:
+//   * scores are formed transposed, S^T = K Q^T, so every lane owns one query
+//     column: the row max / row sum are in-lane reductions plus one exchange
+//     with the partner lane 32 away, and the output O^T = V^T P^T uses the
+//     score registers directly as its B operand (no shuffles, no LDS trip);
+//   * exponentials are exp2 with scale*log2(e) folded into one FMA, and the
+//     stored L is converted back to the natural-log convention (lecture notes
+//     "A2 系统" at courses-9tz.pages.dev/llm/systems, section "从公式到 Triton 程序");
+//   * V is stored transposed in LDS so each A-operand fragment is one
+//     16-byte read; rows are padded by 16 bytes to spread LDS banks;
+//   * the next K/V tile is loaded into registers while the current one is
+//     being used (global loads overlap the matrix-core work);
+//   * workgroups are dispatched longest-first (highest query tile first) so
+//     the short causal tiles fill in the tail.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+template <typename T, int D_, int NQB_, int BK_>
+struct FwdTile {
+    static constexpr int D = D_, NQB = NQB_, BK = BK_;
+    static constexpr int NW = 4, NT = NW * kWave;
+    static constexpr int BQ = NW * NQB * 32;          // queries per workgroup
+    static constexpr int KPL = Mma<T>::KPL;
+    static constexpr int NSD = D / 2 / KPL;           // MFMAs over d per 32x32 block
+    static constexpr int NKB = BK / 32;               // 32-key blocks per tile
+    static constexpr int DP = (D + 31) / 32 * 32;     // d padded to whole 32-row blocks
+    static constexpr int ND = DP / 32;
+    static constexpr int NI = 16 / KPL;               // MFMAs per 32-key reduction block
+    static constexpr int PAD = 16 / sizeof(T);
+    static constexpr int LDK = D + PAD;               // K tile row stride (elements)
+    static constexpr int LDV = BK + PAD;              // V^T tile row stride
+    static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
+};
+
+template <typename T, typename C>
+__global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                    const T *__restrict__ v, T *__restrict__ o,
+                                                    float *__restrict__ lse, int BH, int S, float c,
+                                                    int causal, int nqt) {
+    using M = Mma<T>;
+    using frag = typename M::frag;
+    constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
+    __shared__ __attribute__((aligned(16))) T sK[BK * C::LDK];
+    __shared__ __attribute__((aligned(16))) T sVt[C::DP * C::LDV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int bid = blockIdx.x;
+    const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
+    const int bh = bid % BH;
+    const size_t hoff = (size_t)bh * S * D;
+    q += hoff;
+    k += hoff;
+    v += hoff;
+    o += hoff;
+    lse += (size_t)bh * S;
+    const int q0 = qt * C::BQ;
+    const int qw0 = q0 + wave * NQB * 32;
+
+    if constexpr (C::DP > D) zero_lds_rows<T, C::LDV, C::NT>(sVt, D, C::DP, tid);
+
+    // Q^T fragments (B operand): lane owns query qw0 + 32*qb + l32, d-run of half h.
+    frag qf[NQB][C::NSD];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = qw0 + qb * 32 + l32;
+        if (qi < S)
+            load_run<T, C::NSD>(qf[qb], q + (size_t)qi * D + h * (D / 2));
+        else
+            zero_run<T, C::NSD>(qf[qb]);
+    }
+
+    f32x16 acc[NQB][C::ND];
+    float mrow[NQB], lrow[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        mrow[qb] = -INFINITY;
+        lrow[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db) acc[qb][db] = f32x16{};
+    }
+
+    const int qend = min(q0 + C::BQ, S);
+    int nkt = (S + BK - 1) / BK;
+    if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
+
+    TileIO<T, BK, D, C::NT> kio, vio;
+    kio.load(k, 0, S, tid);
+    vio.load(v, 0, S, tid);
+
+    for (int j = 0; j < nkt; ++j) {
+        const int j0 = j * BK;
+        kio.template store_rows<C::LDK>(sK, tid);
+        vio.template store_cols<C::LDV>(sVt, tid);
+        __syncthreads();
+        if (j + 1 < nkt) {
+            kio.load(k, j0 + BK, S, tid);
+            vio.load(v, j0 + BK, S, tid);
+        }
+        const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
+        if (active) {
+            // S^T block (kb, qb): rows = keys j0 + 32*kb + idx_of(r, h), col = query.
+            f32x16 s[NQB][C::NKB];
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                frag kf[C::NSD];
+                load_run<T, C::NSD>(kf, sK + (kb * 32 + sigma(l32)) * C::LDK + h * (D / 2));
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    f32x16 t = f32x16{};
+#pragma unroll
+                    for (int st = 0; st < C::NSD; ++st) t = M::run(kf[st], qf[qb][st], t);
+                    s[qb][kb] = t;
+                }
+            }
+            const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
+            if (need_mask) {
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    const int qi = qw0 + qb * 32 + l32;
+#pragma unroll
+                    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = j0 + kb * 32 + idx_of(r, h);
+                            if ((causal && key > qi) || key >= S) s[qb][kb][r] = -INFINITY;
+                        }
+                }
+            }
+            // Online softmax (base 2, scores scaled by c = scale*log2 e).
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+                mx = wave_xor32_max(mx);
+                const float mnew = fmaxf(mrow[qb], mx * c);
+                const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+                const float alpha = fast_exp2(mrow[qb] - muse);
+                float ps = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float p = fast_exp2(fmaf(s[qb][kb][r], c, -muse));
+                        s[qb][kb][r] = p;
+                        ps += p;
+                    }
+                lrow[qb] = lrow[qb] * alpha + ps;
+                mrow[qb] = mnew;
+#pragma unroll
+                for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
+            }
+            // O^T += V^T P^T
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+                frag pf[NQB][C::NI];
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) to_bfrag<T>(pf[qb], s[qb][kb]);
+#pragma unroll
+                for (int db = 0; db < C::ND; ++db) {
+                    frag vf[C::NI];
+                    load_kblock<T>(vf, sVt + (db * 32 + sigma(l32)) * C::LDV + kb * 32, h);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                        for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(vf[i], pf[qb][i], acc[qb][db]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: O = acc / l, L = (m + log2 l) * ln 2 (natural log of the scaled scores).
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = qw0 + qb * 32 + l32;
+        const float lt = wave_xor32_sum(lrow[qb]);
+        if (qi < S) {
+            const float inv = 1.f / lt;
+#pragma unroll
+            for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+                for (int hr = 0; hr < 2; ++hr) {
+                    const int d0 = db * 32 + 16 * hr + 8 * h;
+                    if (d0 < D) store8<T>(o + (size_t)qi * D + d0, acc[qb][db], 8 * hr, inv);
+                }
+            if (h == 0) lse[qi] = (mrow[qb] + log2f(lt)) * kLn2;
+        }
+    }
+}
+
+template <typename T, typename C>
+static int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int BH, int S,
+                   float scale, int causal, hipStream_t stream) {
+    const int nqt = (S + C::BQ - 1) / C::BQ;
+    const long long grid = (long long)nqt * BH;
+    if (grid > 0x7fffffffLL) return -1;
+    hipLaunchKernelGGL((fwd_kernel<T, C>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, (T *)o, lse, BH, S, scale * kLog2e,
+                       causal, nqt);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+template <typename T, int D>
+static int fwd_for(const void *q, const void *k, const void *v, void *o, float *lse, int BH, int S,
+                   float scale, int causal, hipStream_t stream) {
+    return run_fwd<T, FwdTile<T, D, 1, 64>>(q, k, v, o, lse, BH, S, scale, causal, stream);
+}
+
+template <typename T>
+static int fwd_dispatch(int D, const void *q, const void *k, const void *v, void *o, float *lse,
+                        int BH, int S, float scale, int causal, hipStream_t stream) {
+    switch (D) {
+    case 16: return fwd_for<T, 16>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    case 32: return fwd_for<T, 32>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    case 64: return fwd_for<T, 64>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    case 80: return fwd_for<T, 80>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    case 96: return fwd_for<T, 96>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    case 128: return fwd_for<T, 128>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    default: return -2;
+    }
+}
+
+int launch_fwd(int dtype, const void *q, const void *k, const void *v, void *o, float *lse, int BH,
+               int S, int D, float scale, int causal, hipStream_t stream) {
+    if (dtype == 1) return fwd_dispatch<bf16>(D, q, k, v, o, lse, BH, S, scale, causal, stream);
+    if (dtype == 0) return fwd_dispatch<float>(D, q, k, v, o, lse, BH, S, scale, causal, stream);
+    return -2;
+}
+
+}  // namespace fa

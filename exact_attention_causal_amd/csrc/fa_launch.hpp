@@ -1,0 +1,30 @@
+// fa_launch.hpp -- internal interface between the C ABI (argument checks)
+// and the kernel translation units (tile selection and launches).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+// Head dimensions with built kernels.
+constexpr int kHeadDims[] = {16, 32, 64, 80, 96, 128};
+
+inline bool head_dim_supported(int D) {
+    for (int d : kHeadDims)
+        if (d == D) return true;
+    return false;
+}
+
+// Each returns 0 on success, -2 (unsupported D/dtype) or -5 (launch refused).
+// Sizes are already validated; BH = B*H.
+int launch_fwd(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
+               int BH, int S, int D, float scale, int causal, hipStream_t stream);
+
+int launch_delta(int dtype, const void *o, const void *dout, float *delta, int BH, int S, int D,
+                 hipStream_t stream);
+
+int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
+               const float *lse, const float *delta, void *dq, void *dk, void *dv, int BH,
+               int S, int D, float scale, int causal, hipStream_t stream);
+
+}  // namespace fa

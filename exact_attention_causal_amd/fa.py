@@ -1,0 +1,171 @@
+"""ctypes binding of the gfx950 attention library (include/fa.h).
+
+The functions named like the C entry points (fa_fwd, fa_bwd_preprocess,
+fa_bwd_workspace_size, fa_bwd, fa_strerror) only marshal arguments: tensors
+become device pointers, the stream becomes HIP's stream handle, and the status
+code comes back unchanged.  ``forward`` / ``backward`` / ``attention_fwd_bwd``
+are conveniences that allocate outputs with PyTorch (device memory is the
+only thing PyTorch provides here) and raise on a non-zero status.
+
+There is no fallback: if the shared library has not been built, or the
+tensors are not on a GPU, every call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
+
+FA_F32 = 0
+FA_BF16 = 1
+FA_OK = 0
+FA_EINVAL = -1
+FA_EUNSUPPORTED = -2
+FA_EALIGN = -3
+FA_EWORKSPACE = -4
+FA_EHIP = -5
+
+#: head dimensions with built kernels
+HEAD_DIMS = (16, 32, 64, 80, 96, 128)
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {fa_strerror(status)}")
+
+
+def load_library():
+    """Load libfa_mi355x.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m exact_attention_causal_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.fa_fwd.restype = _i
+    lib.fa_bwd_preprocess.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+    lib.fa_bwd_preprocess.restype = _i
+    lib.fa_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [_vp] * 10 + [ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.fa_bwd.restype = _i
+    lib.fa_strerror.argtypes = [_i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------- C entry points ---
+
+def fa_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream=None):
+    return load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D,
+                                 float(scale), int(causal), int(dtype), _stream(stream))
+
+
+def fa_bwd_preprocess(o, dout, delta, B, H, S, D, dtype, stream=None):
+    return load_library().fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(delta), B, H, S, D,
+                                            int(dtype), _stream(stream))
+
+
+def fa_bwd_workspace_size(B, H, S, D, dtype):
+    return int(load_library().fa_bwd_workspace_size(B, H, S, D, int(dtype)))
+
+
+def fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes, B, H, S, D, scale,
+           causal, dtype, stream=None):
+    return load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 int(workspace_bytes), B, H, S, D, float(scale), int(causal),
+                                 int(dtype), _stream(stream))
+
+
+def fa_strerror(status):
+    return load_library().fa_strerror(int(status)).decode()
+
+
+# ------------------------------------------------------------ helpers ---
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return FA_BF16
+    if t == torch.float32:
+        return FA_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _check(status, where):
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, S, D] tensors")
+    if not q.is_cuda:
+        raise ValueError("tensors must be on a GPU (there is no CPU path)")
+    return tuple(q.shape)
+
+
+def forward(q, k, v, causal=True, scale=None, out=None, lse=None, stream=None):
+    """O, L for contiguous [B, H, S, D] q, k, v (bf16 or fp32) on the GPU."""
+    B, H, S, D = _shape(q)
+    q, k, v = (x.contiguous() for x in (q, k, v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), device=q.device, dtype=torch.float32)
+    _check(fa_fwd(q, k, v, out, lse, B, H, S, D, scale, causal, dtype_code(q.dtype), stream),
+           "fa_fwd")
+    return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal=True, scale=None, delta=None, grads=None,
+             workspace=None, stream=None):
+    """dQ, dK, dV (and delta) for the forward pass that produced o, lse."""
+    B, H, S, D = _shape(q)
+    q, k, v, o, dout = (x.contiguous() for x in (q, k, v, o, dout))
+    code = dtype_code(q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if delta is None:
+        delta = torch.empty((B, H, S), device=q.device, dtype=torch.float32)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check(fa_bwd_preprocess(o, dout, delta, B, H, S, D, code, stream), "fa_bwd_preprocess")
+    ws_bytes = fa_bwd_workspace_size(B, H, S, D, code)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    _check(fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, ws_bytes, B, H, S, D, scale,
+                  causal, code, stream), "fa_bwd")
+    return dq, dk, dv, delta

@@ -1,0 +1,111 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact causal attention library
+ *         (FlashAttention-2 forward and backward).
+ *
+ * The operations are the ones the CS336 Assignment 2 handout states in
+ * section 4.2 "FlashAttention-2" (videobook.pages.dev, Stanford-CS336 A2):
+ *
+ *   forward   (Eq. 4-6, Eq. 12, Algorithm 1)
+ *       S = Q K^T * scale,  P = softmax_row(S)  (causal: key j allowed iff j <= i),
+ *       O = P V,            L_i = log sum_j exp(S_ij)   (natural log, scaled scores)
+ *   backward  (Eq. 13-19, Algorithm 2)
+ *       D_i = rowsum(O o dO)_i,  P_ij = exp(S_ij - L_i),
+ *       dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
+ *       dQ = dS K * scale,  dK = dS^T Q * scale
+ *
+ * Layout.  Every matrix argument (q, k, v, o, dout, dq, dk, dv) is one
+ * contiguous row-major block [B][H][S][D] of `dtype` elements in device
+ * memory (heads folded into the batch, as in the handout's launch grid
+ * (T_q, batch)); lse and delta are contiguous [B][H][S] fp32.  Queries and
+ * keys share the length S and both start at position 0.
+ *
+ * Ownership.  The caller allocates every buffer (including the backward
+ * workspace, if one is ever needed); the library never allocates, frees,
+ * copies to or from the host, or synchronises.  Outputs are fully
+ * overwritten; inputs must not alias outputs.  All pointers must be device
+ * pointers aligned to 16 bytes.
+ *
+ * Streams and errors.  All work is enqueued on `stream` (0 = the null
+ * stream).  Argument errors are returned synchronously, before anything is
+ * enqueued.  Faults inside a kernel surface at the caller's next stream
+ * synchronisation.  The library holds no mutable state and is thread-safe.
+ *
+ * Supported shapes.  D in {16, 32, 64, 80, 96, 128}; dtype FA_F32 or FA_BF16
+ * (bf16 storage, bf16 matrix-core products with fp32 accumulation; the
+ * softmax statistics, L and D are fp32).  scale must be finite and > 0.
+ * B*H*S*D must fit in 63 bits; S < 2^31.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle (identical to the typedef in hip_runtime_api.h). */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Status codes: 0 = success; negative = error, and nothing was enqueued. */
+enum {
+    FA_OK = 0,
+    FA_EINVAL = -1,       /* null pointer, B/H/S <= 0, causal not 0/1, scale <= 0 or not finite, size overflow */
+    FA_EUNSUPPORTED = -2, /* D or dtype not built */
+    FA_EALIGN = -3,       /* a pointer is not 16-byte aligned */
+    FA_EWORKSPACE = -4,   /* workspace smaller than fa_bwd_workspace_size() */
+    FA_EHIP = -5          /* the HIP runtime refused a launch */
+};
+
+/*
+ * Forward pass (handout section 4.2.2, Algorithm 1; Eq. 4-6 and 12).
+ *   q, k, v : [B][H][S][D] inputs          o   : [B][H][S][D] output
+ *   lse     : [B][H][S] fp32 output, L_i = ln sum_{j allowed} exp(scale * q_i . k_j)
+ *   causal  : 1 = key j is used by query i only when j <= i; 0 = all keys.
+ * Tiles of keys that lie wholly above the diagonal are never visited.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int S, int D, float scale, int causal, fa_dtype dtype,
+           hipStream_t stream);
+
+/*
+ * Backward preprocessing (handout Algorithm 2, its first step, and the text
+ * before Eq. 13): delta_i = sum_d o_id * dout_id, accumulated in fp32 from
+ * the stored forward output o.
+ *   o, dout : [B][H][S][D] inputs          delta : [B][H][S] fp32 output
+ */
+int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
+                      int B, int H, int S, int D, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (0 = none; the
+ * current backward needs none: dK/dV and dQ are each owned by one
+ * workgroup, so no partial sums leave the chip).  Returns 0 for invalid
+ * sizes as well; fa_bwd reports those.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
+
+/*
+ * Backward pass (handout section 4.2.3, Algorithm 2; Eq. 13-19), with the
+ * probabilities recomputed from lse:
+ *   q, k, v, dout : [B][H][S][D] inputs    lse, delta : [B][H][S] fp32 inputs
+ *   dq, dk, dv    : [B][H][S][D] outputs
+ *   workspace     : may be NULL when fa_bwd_workspace_size() is 0.
+ * `scale` and `causal` must be the values the forward pass used.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *dout,
+           const float *lse, const float *delta, void *dq, void *dk, void *dv,
+           void *workspace, size_t workspace_bytes,
+           int B, int H, int S, int D, float scale, int causal, fa_dtype dtype,
+           hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char *fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

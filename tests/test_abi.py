@@ -1,0 +1,118 @@
+"""C-ABI contract checks that run without a GPU.
+
+The library must load, export every entry point include/fa.h declares, and
+reject invalid arguments synchronously, before any device work.  Every call
+below carries at least one invalid argument, so nothing is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+fa = pytest.importorskip("exact_attention_causal_amd.fa")
+
+# fake device addresses: never dereferenced, because each call fails validation
+P = 0x100000          # 16-byte aligned
+MIS = 0x100008        # 8-byte aligned only
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa_mi355x.so is not built (run __graft_entry__.build())")
+    return fa.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_preprocess", "fa_bwd_workspace_size",
+                                     "fa_fwd", "fa_strerror"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(fa.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert fa.fa_strerror(code)
+    assert fa.fa_strerror(0) == "success"
+    assert "unknown" in fa.fa_strerror(17)
+
+
+def test_workspace_size_is_zero(lib):
+    assert fa.fa_bwd_workspace_size(1, 16, 65536, 128, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_size(4, 12, 512, 64, fa.FA_F32) == 0
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, S=128, D=64, scale=0.125, causal=1,
+             dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_fwd(**a)
+
+
+def _pre(**kw):
+    a = dict(o=P, dout=P, delta=P, B=1, H=2, S=128, D=64, dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_bwd_preprocess(**a)
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, dout=P, lse=P, delta=P, dq=P, dk=P, dv=P, workspace=None,
+             workspace_bytes=0, B=1, H=2, S=128, D=64, scale=0.125, causal=1, dtype=fa.FA_BF16,
+             stream=0)
+    a.update(kw)
+    return fa.fa_bwd(**a)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), fa.FA_EINVAL), (dict(lse=None), fa.FA_EINVAL),
+    (dict(B=0), fa.FA_EINVAL), (dict(H=-1), fa.FA_EINVAL), (dict(S=0), fa.FA_EINVAL),
+    (dict(causal=2), fa.FA_EINVAL), (dict(scale=0.0), fa.FA_EINVAL),
+    (dict(scale=-0.1), fa.FA_EINVAL), (dict(scale=float("nan")), fa.FA_EINVAL),
+    (dict(scale=float("inf")), fa.FA_EINVAL),
+    (dict(D=72), fa.FA_EUNSUPPORTED), (dict(D=256), fa.FA_EUNSUPPORTED),
+    (dict(dtype=7), fa.FA_EUNSUPPORTED),
+    (dict(q=MIS), fa.FA_EALIGN), (dict(o=MIS), fa.FA_EALIGN), (dict(lse=MIS), fa.FA_EALIGN),
+    (dict(B=1 << 20, H=1 << 10, S=1 << 20, D=128), fa.FA_EINVAL),
+])
+def test_fwd_rejects(lib, bad, code):
+    assert _fwd(**bad) == code
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(o=None), fa.FA_EINVAL), (dict(delta=None), fa.FA_EINVAL), (dict(S=-5), fa.FA_EINVAL),
+    (dict(D=48), fa.FA_EUNSUPPORTED), (dict(dtype=3), fa.FA_EUNSUPPORTED),
+    (dict(dout=MIS), fa.FA_EALIGN), (dict(delta=P + 4), fa.FA_EALIGN),
+])
+def test_preprocess_rejects(lib, bad, code):
+    assert _pre(**bad) == code
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(dq=None), fa.FA_EINVAL), (dict(delta=None), fa.FA_EINVAL), (dict(H=0), fa.FA_EINVAL),
+    (dict(causal=-1), fa.FA_EINVAL), (dict(scale=float("-inf")), fa.FA_EINVAL),
+    (dict(D=100), fa.FA_EUNSUPPORTED), (dict(dtype=2), fa.FA_EUNSUPPORTED),
+    (dict(dk=MIS), fa.FA_EALIGN), (dict(lse=P + 2), fa.FA_EALIGN),
+])
+def test_bwd_rejects(lib, bad, code):
+    assert _bwd(**bad) == code
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Error metric (per tensor): max |gpu - oracle| / max |oracle|; L is compared
+in absolute terms.  Bounds: bf16 O 2e-2, dQ/dK/dV 5e-2; fp32 O and grads
+1e-4; L 1e-3 absolute.
+
+Small and mid workloads are compared element by element on every output.
+The two long workloads (S = 16000, D = 80 and S = 65536, D = 128) run in the
+launch configuration the benchmark times; the oracle evaluates a seeded
+sample of query rows (O, L, dQ) and of key rows (dK, dV, which need the
+oracle's own L and D for every later query of that head), and whole-tensor
+identities that hold at any size are checked on all rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_causal_amd import fa
+from exact_attention_causal_amd.inputs import (WORKLOADS, make_inputs, sample_rows,
+                                               workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {
+    "bf16": dict(o=2e-2, grad=5e-2, lse=1e-3),
+    "f32": dict(o=1e-4, grad=1e-4, lse=1e-3),
+}
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    denom = float(np.max(np.abs(b))) if b.size else 0.0
+    if denom == 0.0:
+        return float(np.max(np.abs(a))) if a.size else 0.0
+    return float(np.max(np.abs(a - b))) / denom
+
+
+def absdiff(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    fa.load_library()
+    return torch.device("cuda:0")
+
+
+def run_gpu(q, k, v, do, causal=True, scale=None):
+    """fwd + preprocess + bwd through the C ABI; returns CPU fp64 numpy arrays."""
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv, delta = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    out = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
+    return {n: t.double().cpu().numpy() for n, t in out.items()}
+
+
+def check_full(q, k, v, do, dtype, causal=True, scale=None, label=""):
+    print(f"[parity] {label} shape={tuple(q.shape)} dtype={dtype} causal={causal}", flush=True)
+    g = run_gpu(q, k, v, do, causal, scale)
+    r = oracle.backward(*(x.double().numpy() for x in (q, k, v, do)), scale=scale,
+                        causal=causal)
+    tol = TOL[dtype]
+    errs = dict(o=rel(g["o"], r["o"]), lse=absdiff(g["lse"], r["lse"]),
+                dq=rel(g["dq"], r["dq"]), dk=rel(g["dk"], r["dk"]), dv=rel(g["dv"], r["dv"]),
+                delta=rel(g["delta"], r["delta_o"]))
+    print(f"[parity] {label} errors {errs}", flush=True)
+    assert errs["o"] <= tol["o"], errs
+    assert errs["lse"] <= tol["lse"], errs
+    for n in ("dq", "dk", "dv"):
+        assert errs[n] <= tol["grad"], (n, errs)
+    # delta is the fp32 rowsum of the GPU's own (rounded) O; it must sit inside the grad budget
+    assert errs["delta"] <= tol["grad"], errs
+    return errs
+
+
+# --------------------------------------------------------- the workloads ---
+
+@pytest.mark.parametrize("name", ["f32_b1h2_s128_d64", "bf16_b4h12_s512_d64",
+                                  "bf16_b4h16_s2048_d64_peaky"])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    q, k, v, do = workload_inputs(w)
+    check_full(q, k, v, do, w.dtype, causal=True, scale=w.scale, label=name)
+
+
+def _sampled_check(w, n_rows, n_key_heads, key_window):
+    """Sampled oracle comparison at full size (the benchmark's launch shapes)."""
+    print(f"[parity] sampled {w.name}", flush=True)
+    q, k, v, do = workload_inputs(w)
+    g = run_gpu(q, k, v, do, causal=True, scale=w.scale)
+    tol = TOL[w.dtype]
+    qn, kn, vn, don = (x.double().numpy().reshape(w.B * w.H, w.S, w.D) for x in (q, k, v, do))
+    go = {n: g[n].reshape(w.B * w.H, w.S, -1) for n in ("o", "dq", "dk", "dv")}
+    glse = g["lse"].reshape(w.B * w.H, w.S)
+
+    # query rows: O, L, dQ
+    pairs = sample_rows(w.B * w.H, w.S, n_rows, tile=128)
+    by_head = {}
+    for hh, i in pairs:
+        by_head.setdefault(hh, []).append(i)
+    o_ref, o_gpu, l_ref, l_gpu, dq_ref, dq_gpu = [], [], [], [], [], []
+    for hh, rows in sorted(by_head.items()):
+        o, lse, dq = oracle.rows(qn[hh], kn[hh], vn[hh], don[hh], rows, scale=w.scale)
+        o_ref.append(o); l_ref.append(lse); dq_ref.append(dq)
+        o_gpu.append(go["o"][hh][rows]); l_gpu.append(glse[hh][rows]); dq_gpu.append(go["dq"][hh][rows])
+    errs = dict(o=rel(np.concatenate(o_gpu), np.concatenate(o_ref)),
+                lse=absdiff(np.concatenate(l_gpu), np.concatenate(l_ref)),
+                dq=rel(np.concatenate(dq_gpu), np.concatenate(dq_ref)))
+
+    # key rows: dK, dV for keys in the last `key_window` positions of a few heads, plus
+    # tile edges; the oracle computes L and D itself for every query those keys see
+    rng = np.random.default_rng(w.seed + 1000)
+    heads = rng.choice(w.B * w.H, size=n_key_heads, replace=False)
+    jmin = w.S - key_window
+    dk_ref, dk_gpu, dv_ref, dv_gpu = [], [], [], []
+    for hh in heads:
+        rows = np.arange(jmin, w.S)
+        o, lse_part, _ = oracle.rows(qn[hh], kn[hh], vn[hh], don[hh], rows, scale=w.scale)
+        lse_full = np.full(w.S, np.nan)
+        del_full = np.full(w.S, np.nan)
+        lse_full[rows] = lse_part
+        del_full[rows] = np.sum(o * don[hh][rows], axis=-1)
+        cols = np.unique(np.concatenate([
+            rng.integers(jmin, w.S, size=32), [jmin, w.S - 1, (w.S - 1) // 128 * 128]]))
+        cols = cols[cols >= jmin]
+        dk, dv = oracle.cols(qn[hh], kn[hh], vn[hh], don[hh], lse_full, del_full, cols,
+                             scale=w.scale)
+        dk_ref.append(dk); dv_ref.append(dv)
+        dk_gpu.append(go["dk"][hh][cols]); dv_gpu.append(go["dv"][hh][cols])
+    errs["dk"] = rel(np.concatenate(dk_gpu), np.concatenate(dk_ref))
+    errs["dv"] = rel(np.concatenate(dv_gpu), np.concatenate(dv_ref))
+
+    # whole-tensor identities (every row): sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per head
+    # (each residual relative to the sum of magnitudes it is made of)
+    dk_sum = go["dk"].sum(axis=1)
+    dv_sum = go["dv"].sum(axis=1)
+    do_sum = don.sum(axis=1)
+    errs["sum_dk"] = float(np.max(np.abs(dk_sum) / np.abs(go["dk"]).sum(axis=1)))
+    errs["sum_dv"] = float(np.max(np.abs(dv_sum - do_sum) / np.abs(go["dv"]).sum(axis=1)))
+    print(f"[parity] sampled {w.name} errors {errs}", flush=True)
+    assert errs["o"] <= tol["o"], errs
+    assert errs["lse"] <= tol["lse"], errs
+    for n in ("dq", "dk", "dv"):
+        assert errs[n] <= tol["grad"], (n, errs)
+    assert errs["sum_dk"] <= tol["grad"], errs
+    assert errs["sum_dv"] <= tol["grad"], errs
+    assert np.all(np.isfinite(g["o"])) and np.all(np.isfinite(g["dq"]))
+    assert np.all(np.isfinite(g["dk"])) and np.all(np.isfinite(g["dv"]))
+
+
+def test_workload_s16000_d80_sampled():
+    # one head's keys are sampled over the whole sequence (the oracle's L and D for all rows)
+    w = WORKLOADS["bf16_b1h32_s16000_d80"]
+    _sampled_check(w, n_rows=256, n_key_heads=1, key_window=w.S)
+
+
+@pytest.mark.slow
+def test_workload_s65536_d128_sampled():
+    _sampled_check(WORKLOADS["bf16_b1h16_s65536_d128"], n_rows=256, n_key_heads=1,
+                   key_window=1024)
+
+
+# ------------------------------------------------------ edges and tails ---
+
+@pytest.mark.parametrize("S", [1, 2, 15, 17, 31, 33, 63, 65, 127, 129, 200, 257])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sequence_tails(S, dtype):
+    q, k, v, do = make_inputs(1, 2, S, 64, dtype, seed=100 + S)
+    check_full(q, k, v, do, dtype, causal=True, label=f"tail S={S}")
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 80, 96, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_dims(D, dtype):
+    q, k, v, do = make_inputs(2, 2, 300, D, dtype, seed=200 + D)
+    check_full(q, k, v, do, dtype, causal=True, label=f"D={D}")
+
+
+@pytest.mark.parametrize("S,D", [(1, 64), (100, 64), (256, 80), (333, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_noncausal(S, D, dtype):
+    q, k, v, do = make_inputs(1, 3, S, D, dtype, seed=300 + S)
+    check_full(q, k, v, do, dtype, causal=False, label=f"noncausal S={S} D={D}")
+
+
+def test_custom_scale_and_peaky_scores():
+    q, k, v, do = make_inputs(1, 2, 257, 64, "bf16", seed=7, qk_mult=3.0)
+    check_full(q, k, v, do, "bf16", causal=True, scale=0.3, label="scale=0.3 peaky")
+
+
+def test_first_query_and_identical_keys():
+    """Closed forms on the GPU: O_0 = V_0; identical keys give the causal prefix mean."""
+    S, D = 300, 64
+    q, k1, v, _ = make_inputs(1, 2, 1, D, "f32", seed=11)
+    q, _, v, _ = make_inputs(1, 2, S, D, "f32", seed=11)
+    k = k1.expand(1, 2, S, D).contiguous()
+    dev = torch.device("cuda:0")
+    o, lse = fa.forward(q.to(dev), k.to(dev), v.to(dev), causal=True)
+    o = o.double().cpu()
+    prefix = torch.cumsum(v.double(), dim=2) / torch.arange(1, S + 1, dtype=torch.float64)[:, None]
+    assert torch.max(torch.abs(o - prefix)).item() <= 1e-4
+    assert torch.max(torch.abs(o[:, :, 0] - v[:, :, 0].double())).item() <= 1e-6
+
+
+def test_noncontiguous_inputs():
+    q, k, v, do = make_inputs(1, 130, 2, 64, "bf16", seed=12)   # [B, S, H, D] drawn
+    qt, kt, vt, dot = (x.transpose(1, 2) for x in (q, k, v, do))  # -> [B, H, S, D] views
+    check_full(qt, kt, vt, dot, "bf16", causal=True, label="non-contiguous")
+
+
+def test_backward_is_deterministic():
+    q, k, v, do = make_inputs(1, 4, 1000, 80, "bf16", seed=13)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd)
+    first = fa.backward(qd, kd, vd, o, lse, dod)
+    for _ in range(3):
+        again = fa.backward(qd, kd, vd, o, lse, dod)
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+
+
+def test_forward_on_a_side_stream():
+    q, k, v, do = make_inputs(2, 2, 200, 64, "bf16", seed=14)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    ref, _ = fa.forward(qd, kd, vd)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, _ = fa.forward(qd, kd, vd, stream=s)
+    s.synchronize()
+    assert torch.equal(o, ref)
