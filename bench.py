@@ -41,8 +41,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
+    ap.add_argument("--cpu-tokens", type=int, default=12288,
                     help="sequence prefix the CPU oracle baseline runs on")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
+                         "its HBM counters calibrate the traffic figures")
     return ap.parse_args()
 
 
@@ -81,8 +84,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return
+    w = WORKLOADS[args.workload]
     fa.load_library()
     code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
     B, H, S, D = w.shape
