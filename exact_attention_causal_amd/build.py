@@ -23,6 +23,9 @@ CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results go straight to VGPRs (no AGPR round trips for the
+    # softmax and rescale work done on the accumulators)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-ffp-contract=fast", "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]

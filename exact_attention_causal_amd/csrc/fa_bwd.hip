@@ -15,10 +15,11 @@
 //
 // Register/LDS mapping (see fa_common.hpp): in the key-outer pass the scores
 // are formed as S = Q K^T so that each lane owns one key column; P and dS
-// then feed dV^T = dO^T P and dK^T = Q^T dS directly as B operands, with
-// Q^T and dO^T staged transposed in LDS.  In the query-outer pass the scores
-// are S^T = K Q^T (each lane owns one query), and dS^T feeds
-// dQ^T = K^T dS^T with K^T staged transposed in LDS.
+// then feed dV^T = dO^T P and dK^T = Q^T dS directly as B operands, with the
+// Q^T and dO^T operands read out of the row-major Q and dO tiles by the
+// transposing LDS read.  In the query-outer pass the scores are S^T = K Q^T
+// (each lane owns one query), and dS^T feeds dQ^T = K^T dS^T, K^T again read
+// transposed from the row-major K tile.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -75,12 +76,10 @@ struct KvTile {
     static constexpr int NQ2 = BQ2 / 32;              // 32-query blocks per query tile
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;
-    static constexpr int DP = (D + 31) / 32 * 32;
-    static constexpr int ND = DP / 32;
+    static constexpr int ND = (D + 31) / 32;
     static constexpr int NI = 16 / KPL;
-    static constexpr int PAD = 16 / sizeof(T);
-    static constexpr int LDR = D + PAD;               // row-major Q / dO tile stride
-    static constexpr int LDT = BQ2 + PAD;             // transposed Q^T / dO^T tile stride
+    using SW = Swz<T, D>;
+    static constexpr int TILE = BQ2 * SW::PITCH;      // elements per Q or dO tile
     static_assert(D % 16 == 0 && BQ2 % 32 == 0, "tile shape");
 };
 
@@ -94,10 +93,8 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, BQ2 = C::BQ2;
-    __shared__ __attribute__((aligned(16))) T sQ[BQ2 * C::LDR];
-    __shared__ __attribute__((aligned(16))) T sdO[BQ2 * C::LDR];
-    __shared__ __attribute__((aligned(16))) T sQt[C::DP * C::LDT];
-    __shared__ __attribute__((aligned(16))) T sdOt[C::DP * C::LDT];
+    __shared__ __attribute__((aligned(16))) T sQ[C::TILE];
+    __shared__ __attribute__((aligned(16))) T sdO[C::TILE];
     __shared__ __attribute__((aligned(16))) float sL[BQ2];
     __shared__ __attribute__((aligned(16))) float sDl[BQ2];
 
@@ -119,9 +116,9 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     const int kw0 = k0 + wave * 32;
     const int key = kw0 + l32;  // this lane's key column
 
-    if constexpr (C::DP > D) {
-        zero_lds_rows<T, C::LDT, C::NT>(sQt, D, C::DP, tid);
-        zero_lds_rows<T, C::LDT, C::NT>(sdOt, D, C::DP, tid);
+    if constexpr (C::SW::CPR != C::SW::PCH) {
+        zero_lds<T, C::TILE, C::NT>(sQ, tid);
+        zero_lds<T, C::TILE, C::NT>(sdO, tid);
     }
 
     // K^T and V^T fragments (B operands): lane owns key `key`, d-run of half h.
@@ -133,6 +130,8 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         zero_run<T, C::NSD>(kf);
         zero_run<T, C::NSD>(vf);
     }
+    TransReader<T, D> tr;
+    tr.init(lane);
 
     f32x16 dK[C::ND], dV[C::ND];
 #pragma unroll
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     const int nq2 = (S + BQ2 - 1) / BQ2;
     const int i0 = causal ? k0 / BQ2 : 0;
 
-    TileIO<T, BQ2, D, C::NT> qio, dio;
+    TileLoader<T, D, BQ2, C::NT> qio, dio;
     float lreg = 0.f, dreg = 0.f;
     auto prefetch = [&](int qt) {
         qio.load(q, qt * BQ2, S, tid);
@@ -157,13 +156,12 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         }
     };
     if (i0 < nq2) prefetch(i0);
+    if constexpr (C::SW::CPR != C::SW::PCH) __syncthreads();
 
     for (int it = i0; it < nq2; ++it) {
         const int q0 = it * BQ2;
-        qio.template store_rows<C::LDR>(sQ, tid);
-        qio.template store_cols<C::LDT>(sQt, tid);
-        dio.template store_rows<C::LDR>(sdO, tid);
-        dio.template store_cols<C::LDT>(sdOt, tid);
+        qio.store(sQ, tid);
+        dio.store(sdO, tid);
         if (tid < BQ2) {
             sL[tid] = lreg;
             sDl[tid] = dreg;
@@ -180,13 +178,13 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                 f32x16 s = f32x16{}, dp = f32x16{};
                 {
                     frag qa[C::NSD];
-                    load_run<T, C::NSD>(qa, sQ + (qb * 32 + sigma(l32)) * C::LDR + h * (D / 2));
+                    load_row_frags<T, D>(qa, sQ, qb * 32 + sigma(l32), h);
 #pragma unroll
                     for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], kf[st], s);
                 }
                 {
                     frag da[C::NSD];
-                    load_run<T, C::NSD>(da, sdO + (qb * 32 + sigma(l32)) * C::LDR + h * (D / 2));
+                    load_row_frags<T, D>(da, sdO, qb * 32 + sigma(l32), h);
 #pragma unroll
                     for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], vf[st], dp);
                 }
@@ -206,12 +204,15 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                         dl[8 * hr + 4 + t] = d1[t];
                     }
                 }
+                // query q0 + 32*qb + idx_of(r, h) is kept iff it is at least `lo` and below `hi`
+                const int lo = (causal ? key : 0) - q0 - 32 * qb - 8 * h;
+                const int hi = S - q0 - 32 * qb - 8 * h;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float p = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
                     if (need_mask) {
-                        const int qi = q0 + qb * 32 + idx_of(r, h);
-                        if ((causal && key > qi) || qi >= S) p = 0.f;
+                        const int e = 16 * (r / 8) + (r % 8);
+                        p = (e >= lo && e < hi) ? p : 0.f;
                     }
                     s[r] = p;
                     dp[r] = p * (dp[r] - dl[r]);  // Eq. 17
@@ -221,12 +222,11 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                 to_bfrag<T>(sf, dp);
 #pragma unroll
                 for (int db = 0; db < C::ND; ++db) {
-                    const int arow = (db * 32 + sigma(l32)) * C::LDT + qb * 32;
                     frag a[C::NI];
-                    load_kblock<T>(a, sdOt + arow, h);
+                    tr.load(a, sdO, qb, db, lane);
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) dV[db] = M::run(a[i], pf[i], dV[db]);  // Eq. 15
-                    load_kblock<T>(a, sQt + arow, h);
+                    tr.load(a, sQ, qb, db, lane);
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) dK[db] = M::run(a[i], sf[i], dK[db]);  // Eq. 19
                 }
@@ -259,12 +259,10 @@ struct QTile {
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;
     static constexpr int NKB = BK / 32;
-    static constexpr int DP = (D + 31) / 32 * 32;
-    static constexpr int ND = DP / 32;
+    static constexpr int ND = (D + 31) / 32;
     static constexpr int NI = 16 / KPL;
-    static constexpr int PAD = 16 / sizeof(T);
-    static constexpr int LDR = D + PAD;               // row-major K / V tile stride
-    static constexpr int LDT = BK + PAD;              // transposed K^T tile stride
+    using SW = Swz<T, D>;
+    static constexpr int TILE = BK * SW::PITCH;       // elements per K or V tile
     static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
 };
 
@@ -278,9 +276,8 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
-    __shared__ __attribute__((aligned(16))) T sK[BK * C::LDR];
-    __shared__ __attribute__((aligned(16))) T sV[BK * C::LDR];
-    __shared__ __attribute__((aligned(16))) T sKt[C::DP * C::LDT];
+    __shared__ __attribute__((aligned(16))) T sK[C::TILE];
+    __shared__ __attribute__((aligned(16))) T sV[C::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
@@ -298,7 +295,10 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     const int q0 = qt * C::BQ;
     const int qw0 = q0 + wave * NQB * 32;
 
-    if constexpr (C::DP > D) zero_lds_rows<T, C::LDT, C::NT>(sKt, D, C::DP, tid);
+    if constexpr (C::SW::CPR != C::SW::PCH) {
+        zero_lds<T, C::TILE, C::NT>(sK, tid);
+        zero_lds<T, C::TILE, C::NT>(sV, tid);
+    }
 
     // Q^T, dO^T fragments (B operands) and the row statistics of this lane's query.
     frag qf[NQB][C::NSD], df[NQB][C::NSD];
@@ -318,6 +318,8 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
             dl[qb] = 0.f;
         }
     }
+    TransReader<T, D> tr;
+    tr.init(lane);
 
     f32x16 acc[NQB][C::ND];
 #pragma unroll
@@ -329,15 +331,15 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     int nkt = (S + BK - 1) / BK;
     if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
 
-    TileIO<T, BK, D, C::NT> kio, vio;
+    TileLoader<T, D, BK, C::NT> kio, vio;
     kio.load(k, 0, S, tid);
     vio.load(v, 0, S, tid);
+    if constexpr (C::SW::CPR != C::SW::PCH) __syncthreads();
 
     for (int j = 0; j < nkt; ++j) {
         const int j0 = j * BK;
-        kio.template store_rows<C::LDR>(sK, tid);
-        kio.template store_cols<C::LDT>(sKt, tid);
-        vio.template store_rows<C::LDR>(sV, tid);
+        kio.store(sK, tid);
+        vio.store(sV, tid);
         __syncthreads();
         if (j + 1 < nkt) {
             kio.load(k, j0 + BK, S, tid);
@@ -349,8 +351,8 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 frag ka[C::NSD], va[C::NSD];
-                load_run<T, C::NSD>(ka, sK + (kb * 32 + sigma(l32)) * C::LDR + h * (D / 2));
-                load_run<T, C::NSD>(va, sV + (kb * 32 + sigma(l32)) * C::LDR + h * (D / 2));
+                load_row_frags<T, D>(ka, sK, kb * 32 + sigma(l32), h);
+                load_row_frags<T, D>(va, sV, kb * 32 + sigma(l32), h);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     // S^T block: rows = keys j0 + 32*kb + idx_of(r, h), col = query.
@@ -360,13 +362,11 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
                     for (int st = 0; st < C::NSD; ++st) dp = M::run(va[st], df[qb][st], dp);
                     const int qi = qw0 + qb * 32 + l32;
+                    const int t = (causal ? min(qi + 1, S) : S) - j0 - 32 * kb - 8 * h;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float p = fast_exp2(fmaf(s[r], c, -lq[qb]));  // Eq. 14
-                        if (need_mask) {
-                            const int kk = j0 + kb * 32 + idx_of(r, h);
-                            if ((causal && kk > qi) || kk >= S) p = 0.f;
-                        }
+                        if (need_mask) p = (16 * (r / 8) + (r % 8) < t) ? p : 0.f;
                         dp[r] = p * (dp[r] - dl[qb]);  // Eq. 17
                     }
                     frag sf[C::NI];
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
                     for (int db = 0; db < C::ND; ++db) {
                         frag a[C::NI];
-                        load_kblock<T>(a, sKt + (db * 32 + sigma(l32)) * C::LDT + kb * 32, h);
+                        tr.load(a, sK, kb, db, lane);
 #pragma unroll
                         for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(a[i], sf[i], acc[qb][db]);  // Eq. 18
                     }
@@ -415,8 +415,7 @@ template <typename T, int D>
 static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                    const float *delta, void *dq, void *dk, void *dv, int BH, int S, float scale,
                    int causal, hipStream_t stream) {
-    // fp32 tiles are twice the bytes: halve the query tile of the key-outer pass for wide heads
-    using KC = KvTile<T, D, (sizeof(T) == 4 && D > 64) ? 32 : 64>;
+    using KC = KvTile<T, D, 64>;
     using QC = QTile<T, D, 1, 64>;
     const float c = scale * kLog2e;
     const long long g1 = (long long)((S + KC::BKV - 1) / KC::BKV) * BH;

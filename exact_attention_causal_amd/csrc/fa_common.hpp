@@ -94,22 +94,6 @@ __device__ inline void zero_run(typename Mma<T>::frag (&dst)[N]) {
     for (int i = 0; i < N; ++i) dst[i] = Mma<T>::zero();
 }
 
-// A-operand fragments reducing over one 32-index block of a transposed LDS
-// tile row: elements idx_of(r, h) for r = 0..15, i.e. runs [8h, 8h+8) and
-// [16+8h, 24+8h) of `row` (16/KPL instructions).
-template <typename T>
-__device__ inline void load_kblock(typename Mma<T>::frag (&dst)[16 / Mma<T>::KPL], const T *row, int h) {
-    constexpr int H = 8 / Mma<T>::KPL;
-    typename Mma<T>::frag a[H], b[H];
-    load_run<T, H>(a, row + 8 * h);
-    load_run<T, H>(b, row + 16 + 8 * h);
-#pragma unroll
-    for (int i = 0; i < H; ++i) {
-        dst[i] = a[i];
-        dst[H + i] = b[i];
-    }
-}
-
 // An fp32 output block (16 registers) as B-operand fragments (rounded to T).
 template <typename T>
 __device__ inline void to_bfrag(typename Mma<T>::frag (&dst)[16 / Mma<T>::KPL], const f32x16 &c) {
@@ -127,94 +111,147 @@ __device__ inline void to_bfrag(typename Mma<T>::frag (&dst)[16 / Mma<T>::KPL], 
     }
 }
 
-// ---- global <-> registers <-> LDS tiles ------------------------------------
+// ---- swizzled row-major LDS tiles -----------------------------------------
 //
-// A tile is R rows x D columns of a [S][D] head.  It is moved in units of
-// 4 rows x 16 bytes: unit u covers column chunk c = u % CPR (CPR = 16-byte
-// chunks per row) of rows 4*(u / CPR) .. +3, so consecutive threads read
-// consecutive 16-byte chunks of a row.  Rows at or beyond S read as zero.
+// Every LDS tile is row-major with a power-of-two pitch of 8, 16 or 32
+// 16-byte chunks per row, and logical chunk c of row r sits at physical chunk
+// c ^ f(r).  f is chosen so that both read patterns the kernels use are free
+// of bank conflicts on the 64 four-byte LDS banks:
+//   * "row" reads (A operand reducing over columns): 16 lanes read one
+//     16-byte chunk each from 16 different rows;
+//   * "transposed" reads (ds_read_b64_tr_b16, A operand reducing over rows):
+//     32 lanes read 4 consecutive rows x 64 bytes.
+// Chunks at or beyond the logical row length stay zero (the tile is cleared
+// once), which is how head dimensions pad to whole 32-row output blocks.
 
-template <typename T, int R, int D, int NT>
-struct TileIO {
-    static constexpr int VEC = 16 / sizeof(T);       // elements per 16-byte chunk
-    static constexpr int CPR = D / VEC;              // chunks per row
-    static constexpr int UNITS = (R / 4) * CPR;
-    static constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread
-    static_assert(D % VEC == 0, "D must be a multiple of 16 bytes");
-    static_assert(R % 4 == 0, "tile rows must be a multiple of 4");
+template <typename T, int D>
+struct Swz {
+    static constexpr int CW = 16 / sizeof(T);                            // elements per chunk
+    static constexpr int CPR = D / CW;                                   // logical chunks per row
+    static constexpr int PCH = CPR <= 8 ? 8 : (CPR <= 16 ? 16 : 32);     // physical chunks per row
+    static constexpr int PITCH = PCH * CW;                               // elements per row
+    static_assert(D % CW == 0, "rows must be whole 16-byte chunks");
+    __device__ static constexpr inline int f(int r) {
+        return PCH == 8 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : 4 * (r & 3) + ((r >> 2) & 3);
+    }
+    // element offset of logical chunk c of row r
+    __device__ static constexpr inline int off(int r, int c) { return r * PITCH + ((c ^ f(r)) * CW); }
+    // element offset of column `col` of row r
+    __device__ static constexpr inline int at(int r, int col) { return off(r, col / CW) + col % CW; }
+};
 
-    u32x4 reg[UPT][4];
+// Global -> registers -> LDS mover for an R-row tile of a [S][D] head.
+// Unit u is chunk u % CPR of row u / CPR, so consecutive threads read
+// consecutive 16-byte chunks.  Rows at or beyond S read as zero.
+template <typename T, int D, int R, int NT>
+struct TileLoader {
+    using SW = Swz<T, D>;
+    static constexpr int UNITS = R * SW::CPR;
+    static constexpr int UPT = (UNITS + NT - 1) / NT;
+    u32x4 reg[UPT];
 
     __device__ inline void load(const T *base, int row0, int S, int tid) {
 #pragma unroll
         for (int i = 0; i < UPT; ++i) {
             const int u = tid + i * NT;
-            const int c = u % CPR, rg = u / CPR;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = row0 + 4 * rg + rr;
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if ((UNITS % NT == 0 || u < UNITS) && row < S)
-                    x = *reinterpret_cast<const u32x4 *>(base + (size_t)row * D + c * VEC);
-                reg[i][rr] = x;
-            }
+            const int r = u / SW::CPR, c = u % SW::CPR;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if ((UNITS % NT == 0 || u < UNITS) && row0 + r < S)
+                x = *reinterpret_cast<const u32x4 *>(base + (size_t)(row0 + r) * D + c * SW::CW);
+            reg[i] = x;
         }
     }
-
-    // Row-major LDS tile, row stride LD elements.
-    template <int LD>
-    __device__ inline void store_rows(T *lds, int tid) const {
+    __device__ inline void store(T *lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < UPT; ++i) {
             const int u = tid + i * NT;
             if (UNITS % NT != 0 && u >= UNITS) continue;
-            const int c = u % CPR, rg = u / CPR;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                *reinterpret_cast<u32x4 *>(lds + (4 * rg + rr) * LD + c * VEC) = reg[i][rr];
-        }
-    }
-
-    // Transposed LDS tile: element (row, d) goes to lds[d * LD + row].
-    template <int LD>
-    __device__ inline void store_cols(T *lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-            const int u = tid + i * NT;
-            if (UNITS % NT != 0 && u >= UNITS) continue;
-            const int c = u % CPR, rg = u / CPR;
-            if constexpr (sizeof(T) == 2) {
-                // 8 columns of 4 rows: 8 writes of 4 bf16 (8 bytes)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int w = t / 2, sh = 16 * (t % 2);
-                    uint32_t e0 = (reg[i][0][w] >> sh) & 0xffffu, e1 = (reg[i][1][w] >> sh) & 0xffffu;
-                    uint32_t e2 = (reg[i][2][w] >> sh) & 0xffffu, e3 = (reg[i][3][w] >> sh) & 0xffffu;
-                    u32x2 p = {e0 | (e1 << 16), e2 | (e3 << 16)};
-                    *reinterpret_cast<u32x2 *>(lds + (c * 8 + t) * LD + 4 * rg) = p;
-                }
-            } else {
-                // 4 columns of 4 rows: 4 writes of 4 fp32 (16 bytes)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    u32x4 p = {reg[i][0][t], reg[i][1][t], reg[i][2][t], reg[i][3][t]};
-                    *reinterpret_cast<u32x4 *>(lds + (c * 4 + t) * LD + 4 * rg) = p;
-                }
-            }
+            const int r = u / SW::CPR, c = u % SW::CPR;
+            *reinterpret_cast<u32x4 *>(lds + SW::off(r, c)) = reg[i];
         }
     }
 };
 
-// Zero rows [r0, r1) of a row-major LDS array with LD elements per row.
-template <typename T, int LD, int NT>
-__device__ inline void zero_lds_rows(T *lds, int r0, int r1, int tid) {
-    static_assert((LD * sizeof(T)) % 16 == 0, "row stride must be 16-byte aligned");
-    constexpr int CH = LD * sizeof(T) / 16;
-    for (int u = tid; u < (r1 - r0) * CH; u += NT) {
-        const int r = r0 + u / CH, c = u % CH;
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(lds + r * LD) + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+// Clear n elements of LDS (n a multiple of 8 bytes' worth is not required; 16-byte steps).
+template <typename T, int N, int NT>
+__device__ inline void zero_lds(T *lds, int tid) {
+    static_assert((N * sizeof(T)) % 16 == 0, "tile bytes must be a multiple of 16");
+    constexpr int CH = N * sizeof(T) / 16;
+    for (int u = tid; u < CH; u += NT) reinterpret_cast<u32x4 *>(lds)[u] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// A-operand fragments reducing over the head dimension, from rows of a tile:
+// lane (h, l32) takes row `row` and columns [h*D/2, (h+1)*D/2) (D/2/KPL fragments).
+template <typename T, int D>
+__device__ inline void load_row_frags(typename Mma<T>::frag (&dst)[D / 2 / Mma<T>::KPL], const T *tile,
+                                      int row, int h) {
+    using SW = Swz<T, D>;
+    constexpr int KPL = Mma<T>::KPL;
+    constexpr int NCH = D / 2 / SW::CW;  // chunks per half row
+    const T *rp = tile + row * SW::PITCH;
+    const int fx = SW::f(row);
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(rp + (((h * NCH + q) ^ fx) * SW::CW));
+        if constexpr (KPL == 8) {
+            dst[q] = __builtin_bit_cast(bf16x8, x);
+        } else {
+            const f32x4 v = __builtin_bit_cast(f32x4, x);
+            dst[4 * q + 0] = v[0];
+            dst[4 * q + 1] = v[1];
+            dst[4 * q + 2] = v[2];
+            dst[4 * q + 3] = v[3];
+        }
     }
 }
+
+// A-operand fragments reducing over 32 rows of a tile (rows 32*kb + idx_of(r, h)),
+// output row = column 32*cb + sigma(l32).  bf16 uses the LDS transpose read
+// ds_read_b64_tr_b16: in each 16-lane group, destination lane i receives
+// column i of the 4 x 16 block whose row k, columns 4c..4c+3 the source lane
+// 4k + c points at.  fp32 reads single elements.
+template <typename T, int D>
+struct TransReader {
+    using SW = Swz<T, D>;
+    static constexpr int NCB = (D + 31) / 32;  // 32-column output blocks
+    static constexpr int NI = 16 / Mma<T>::KPL;
+    int off[NCB][2];  // bf16: per output block and half-fragment, lane offset within a 16-row slab
+
+    __device__ inline void init(int lane) {
+        if constexpr (Mma<T>::KPL == 8) {
+            const int g = lane >> 4, j = lane & 15, k = j >> 2, c = j & 3;
+            const int h = g >> 1, sub = g & 1;
+            constexpr int perm4[4] = {0, 8, 4, 12};
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int row = 4 * rr + 8 * h + k;          // row within a 16-row slab
+                    const int col = 32 * cb + 16 * sub + perm4[c];
+                    off[cb][rr] = SW::at(row, col);
+                }
+        }
+    }
+
+    __device__ inline void load(typename Mma<T>::frag (&dst)[NI], const T *tile, int kb, int cb, int lane) const {
+        if constexpr (Mma<T>::KPL == 8) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const T *slab = tile + (32 * kb + 16 * u) * SW::PITCH;  // rows 32kb+16u .. +15
+                typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+                const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4 *)(slab + off[cb][0]));
+                const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4 *)(slab + off[cb][1]));
+                dst[u] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            }
+        } else {
+            const int h = lane >> 5, col = 32 * cb + sigma(lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[r] = tile[SW::at(32 * kb + idx_of(r, h), col)];
+        }
+    }
+};
 
 // Store 8 consecutive output elements (fp32 values * mul, rounded to T).
 template <typename T>

@@ -19,8 +19,11 @@
 //   * exponentials are exp2 with scale*log2(e) folded into one FMA, and the
 //     stored L is converted back to the natural-log convention (lecture notes
 //     "A2 系统" at courses-9tz.pages.dev/llm/systems, section "从公式到 Triton 程序");
-//   * V is stored transposed in LDS so each A-operand fragment is one
-//     16-byte read; rows are padded by 16 bytes to spread LDS banks;
+//   * K and V tiles sit row-major in LDS with an XOR swizzle; V^T operand
+//     fragments come straight from the row-major tile through the gfx950
+//     transposing LDS read, so nothing is transposed on the way in;
+//   * the accumulator is rescaled only when a new score exceeds the running
+//     maximum by 2^8 (exactness is kept because O and l share the stale max);
 //   * the next K/V tile is loaded into registers while the current one is
 //     being used (global loads overlap the matrix-core work);
 //   * workgroups are dispatched longest-first (highest query tile first) so
@@ -38,14 +41,17 @@ struct FwdTile {
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;           // MFMAs over d per 32x32 block
     static constexpr int NKB = BK / 32;               // 32-key blocks per tile
-    static constexpr int DP = (D + 31) / 32 * 32;     // d padded to whole 32-row blocks
-    static constexpr int ND = DP / 32;
+    static constexpr int ND = (D + 31) / 32;          // 32-row output blocks over d
     static constexpr int NI = 16 / KPL;               // MFMAs per 32-key reduction block
-    static constexpr int PAD = 16 / sizeof(T);
-    static constexpr int LDK = D + PAD;               // K tile row stride (elements)
-    static constexpr int LDV = BK + PAD;              // V^T tile row stride
+    using SW = Swz<T, D>;
+    static constexpr int TILE = BK * SW::PITCH;       // elements per K or V tile
     static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
 };
+
+// Scores more than 2^kRescaleSlack above the running maximum force a rescale;
+// below that, p = exp2(s - m) stays <= 2^kRescaleSlack, which fp32 and bf16
+// hold exactly as well as values <= 1, and O and l keep the same stale m.
+constexpr float kRescaleSlack = 8.f;
 
 template <typename T, typename C>
 __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
@@ -55,8 +61,8 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
-    __shared__ __attribute__((aligned(16))) T sK[BK * C::LDK];
-    __shared__ __attribute__((aligned(16))) T sVt[C::DP * C::LDV];
+    __shared__ __attribute__((aligned(16))) T sK[C::TILE];
+    __shared__ __attribute__((aligned(16))) T sV[C::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
@@ -72,7 +78,11 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     const int q0 = qt * C::BQ;
     const int qw0 = q0 + wave * NQB * 32;
 
-    if constexpr (C::DP > D) zero_lds_rows<T, C::LDV, C::NT>(sVt, D, C::DP, tid);
+    // padding chunks of each row must read as zero
+    if constexpr (C::SW::CPR != C::SW::PCH) {
+        zero_lds<T, C::TILE, C::NT>(sK, tid);
+        zero_lds<T, C::TILE, C::NT>(sV, tid);
+    }
 
     // Q^T fragments (B operand): lane owns query qw0 + 32*qb + l32, d-run of half h.
     frag qf[NQB][C::NSD];
@@ -84,6 +94,8 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
         else
             zero_run<T, C::NSD>(qf[qb]);
     }
+    TransReader<T, D> vt;
+    vt.init(lane);
 
     f32x16 acc[NQB][C::ND];
     float mrow[NQB], lrow[NQB];
@@ -99,14 +111,15 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     int nkt = (S + BK - 1) / BK;
     if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
 
-    TileIO<T, BK, D, C::NT> kio, vio;
+    TileLoader<T, D, BK, C::NT> kio, vio;
     kio.load(k, 0, S, tid);
     vio.load(v, 0, S, tid);
+    if constexpr (C::SW::CPR != C::SW::PCH) __syncthreads();
 
     for (int j = 0; j < nkt; ++j) {
         const int j0 = j * BK;
-        kio.template store_rows<C::LDK>(sK, tid);
-        vio.template store_cols<C::LDV>(sVt, tid);
+        kio.store(sK, tid);
+        vio.store(sV, tid);
         __syncthreads();
         if (j + 1 < nkt) {
             kio.load(k, j0 + BK, S, tid);
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 frag kf[C::NSD];
-                load_run<T, C::NSD>(kf, sK + (kb * 32 + sigma(l32)) * C::LDK + h * (D / 2));
+                load_row_frags<T, D>(kf, sK, kb * 32 + sigma(l32), h);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     f32x16 t = f32x16{};
@@ -130,19 +143,21 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
             }
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
             if (need_mask) {
+                // key j0 + 32*kb + idx_of(r, h) is kept iff it is below `lim`
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     const int qi = qw0 + qb * 32 + l32;
+                    const int lim = causal ? min(qi + 1, S) : S;
+                    const int t = lim - j0 - 8 * h;
 #pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = j0 + kb * 32 + idx_of(r, h);
-                            if ((causal && key > qi) || key >= S) s[qb][kb][r] = -INFINITY;
-                        }
+                        for (int r = 0; r < 16; ++r)
+                            s[qb][kb][r] = (32 * kb + 16 * (r / 8) + (r % 8) < t) ? s[qb][kb][r] : -INFINITY;
                 }
             }
-            // Online softmax (base 2, scores scaled by c = scale*log2 e).
+            // Online softmax in base 2 (scores scaled by c = scale*log2 e).  The
+            // running maximum only moves when a score exceeds it by kRescaleSlack.
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
                 float mx = -INFINITY;
@@ -150,10 +165,18 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
                 for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-                mx = wave_xor32_max(mx);
-                const float mnew = fmaxf(mrow[qb], mx * c);
-                const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-                const float alpha = fast_exp2(mrow[qb] - muse);
+                mx = wave_xor32_max(mx) * c;
+                const bool grow = mx > mrow[qb] + kRescaleSlack;
+                if (__ballot(grow) != 0) {  // wave-uniform: rare after the first tile
+                    const float mnew = grow ? mx : mrow[qb];
+                    const float alpha = fast_exp2(mrow[qb] - mnew);
+                    lrow[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
+                    mrow[qb] = mnew;
+                }
+                // a row whose maximum is still -inf has seen only masked keys: use 0
+                const float muse = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
                 float ps = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
@@ -163,10 +186,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
                         s[qb][kb][r] = p;
                         ps += p;
                     }
-                lrow[qb] = lrow[qb] * alpha + ps;
-                mrow[qb] = mnew;
-#pragma unroll
-                for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
+                lrow[qb] += ps;
             }
             // O^T += V^T P^T
 #pragma unroll
@@ -177,7 +197,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
 #pragma unroll
                 for (int db = 0; db < C::ND; ++db) {
                     frag vf[C::NI];
-                    load_kblock<T>(vf, sVt + (db * 32 + sigma(l32)) * C::LDV + kb * 32, h);
+                    vt.load(vf, sV, kb, db, lane);
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
