@@ -172,6 +172,64 @@ struct TileLoader {
     }
 };
 
+// Direct global -> LDS tile loads (global_load_lds_dwordx4): each instruction
+// of a wave writes 1 KiB of consecutive LDS (16 bytes per lane, in lane
+// order), so a lane is told which global chunk belongs at its LDS position of
+// the swizzled tile.  Rows past the end of the sequence load the last row and
+// padding chunks load the row's last chunk: the values are finite, and the
+// kernels mask those rows or never store the outputs they feed.
+template <typename T, int D, int R, int NW>
+struct TileDma {
+    using SW = Swz<T, D>;
+    static constexpr int ROW_BYTES = SW::PITCH * (int)sizeof(T);
+    static constexpr int RPI = 1024 / ROW_BYTES;      // rows per instruction
+    static constexpr int NINS = R / RPI;              // instructions per tile
+    static constexpr int IPW = NINS / NW;             // instructions per wave
+    static_assert(1024 % ROW_BYTES == 0 && R % RPI == 0 && NINS % NW == 0, "tile/DMA shape");
+    int row[IPW];  // row within the tile
+    int col[IPW];  // element column of the chunk
+
+    __device__ inline void init(int lane, int wave) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int p = (wave * IPW + i) * 64 + lane;  // 16-byte slot within the tile
+            const int r = p / SW::PCH, pc = p % SW::PCH;
+            const int c = min(pc ^ SW::f(r), SW::CPR - 1);
+            row[i] = r;
+            col[i] = c * SW::CW;
+        }
+    }
+    // Issue this wave's share of the tile holding rows row0 .. row0 + R - 1.
+    __device__ inline void issue(T *lds, const T *base, int row0, int S, int wave) const {
+        typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int r = min(row0 + row[i], S - 1);
+            T *dst = lds + (wave * IPW + i) * (1024 / (int)sizeof(T));
+            __builtin_amdgcn_global_load_lds((const void *)(base + (size_t)r * D + col[i]),
+                                             (lds_void *)dst, 16, 0, 0);
+        }
+    }
+};
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// s_waitcnt lgkmcnt(0) (LDS reads and writes of this wave completed).
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+
+// Workgroup barrier that does not wait for outstanding global loads (so LDS
+// DMA of the next tile stays in flight); the empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ inline void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Clear n elements of LDS (n a multiple of 8 bytes' worth is not required; 16-byte steps).
 template <typename T, int N, int NT>
 __device__ inline void zero_lds(T *lds, int tid) {

@@ -24,8 +24,9 @@
 //     transposing LDS read, so nothing is transposed on the way in;
 //   * the accumulator is rescaled only when a new score exceeds the running
 //     maximum by 2^8 (exactness is kept because O and l share the stale max);
-//   * the next K/V tile is loaded into registers while the current one is
-//     being used (global loads overlap the matrix-core work);
+//   * K/V tiles are loaded straight into LDS (global_load_lds_dwordx4) into
+//     two stages, so the next tile streams in while the current one is used
+//     and no registers or VALU work are spent staging it;
 //   * workgroups are dispatched longest-first (highest query tile first) so
 //     the short causal tiles fill in the tail.
 #include "fa_common.hpp"
@@ -33,10 +34,10 @@
 
 namespace fa {
 
-template <typename T, int D_, int NQB_, int BK_>
+template <typename T, int D_, int NQB_, int BK_, int NW_>
 struct FwdTile {
     static constexpr int D = D_, NQB = NQB_, BK = BK_;
-    static constexpr int NW = 4, NT = NW * kWave;
+    static constexpr int NW = NW_, NT = NW * kWave;
     static constexpr int BQ = NW * NQB * 32;          // queries per workgroup
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;           // MFMAs over d per 32x32 block
@@ -45,6 +46,7 @@ struct FwdTile {
     static constexpr int NI = 16 / KPL;               // MFMAs per 32-key reduction block
     using SW = Swz<T, D>;
     static constexpr int TILE = BK * SW::PITCH;       // elements per K or V tile
+    using DMA = TileDma<T, D, BK, NW>;
     static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
 };
 
@@ -61,10 +63,15 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
-    __shared__ __attribute__((aligned(16))) T sK[C::TILE];
-    __shared__ __attribute__((aligned(16))) T sV[C::TILE];
+    // Two stages of K and V tiles: the next tile streams in while this one is
+    // used.  Each stage is its own array and the loop is unrolled by two, so
+    // the compiler can see that reads of one stage never alias the DMA into
+    // the other and does not wait for the in-flight tile.
+    __shared__ __attribute__((aligned(1024))) T sK0[C::TILE], sK1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sV0[C::TILE], sV1[C::TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
@@ -77,12 +84,6 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     lse += (size_t)bh * S;
     const int q0 = qt * C::BQ;
     const int qw0 = q0 + wave * NQB * 32;
-
-    // padding chunks of each row must read as zero
-    if constexpr (C::SW::CPR != C::SW::PCH) {
-        zero_lds<T, C::TILE, C::NT>(sK, tid);
-        zero_lds<T, C::TILE, C::NT>(sV, tid);
-    }
 
     // Q^T fragments (B operand): lane owns query qw0 + 32*qb + l32, d-run of half h.
     frag qf[NQB][C::NSD];
@@ -111,20 +112,21 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     int nkt = (S + BK - 1) / BK;
     if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
 
-    TileLoader<T, D, BK, C::NT> kio, vio;
-    kio.load(k, 0, S, tid);
-    vio.load(v, 0, S, tid);
-    if constexpr (C::SW::CPR != C::SW::PCH) __syncthreads();
+    typename C::DMA dma;
+    dma.init(lane, wave);
+    dma.issue(sK0, k, 0, S, wave);
+    dma.issue(sV0, v, 0, S, wave);
 
-    for (int j = 0; j < nkt; ++j) {
+    auto step = [&](const T *tK, const T *tV, T *nK, T *nV, int j) {
         const int j0 = j * BK;
-        kio.store(sK, tid);
-        vio.store(sV, tid);
-        __syncthreads();
-        if (j + 1 < nkt) {
-            kio.load(k, j0 + BK, S, tid);
-            vio.load(v, j0 + BK, S, tid);
-        }
+        // Prefetch tile j+1 into the other stage (released by the barrier that
+        // ended the previous step).  It is issued unconditionally -- past the
+        // last tile it re-reads valid rows nobody uses -- because a conditional
+        // issue makes the compiler wait for every DMA before the next LDS read.
+        dma.issue(nK, k, j0 + BK, S, wave);
+        dma.issue(nV, v, j0 + BK, S, wave);
+        wait_vmcnt<2 * C::DMA::IPW>();  // this wave's part of tile j has landed
+        lds_barrier();                  // every wave's part of tile j has landed
         const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
         if (active) {
             // S^T block (kb, qb): rows = keys j0 + 32*kb + idx_of(r, h), col = query.
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 frag kf[C::NSD];
-                load_row_frags<T, D>(kf, sK, kb * 32 + sigma(l32), h);
+                load_row_frags<T, D>(kf, tK, kb * 32 + sigma(l32), h);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     f32x16 t = f32x16{};
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
 #pragma unroll
                 for (int db = 0; db < C::ND; ++db) {
                     frag vf[C::NI];
-                    vt.load(vf, sV, kb, db, lane);
+                    vt.load(vf, tV, kb, db, lane);
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -205,8 +207,14 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
                 }
             }
         }
-        __syncthreads();
+        wait_lgkm0();
+        lds_barrier();  // every wave is done reading this stage
+    };
+    for (int j = 0; j < nkt; j += 2) {
+        step(sK0, sV0, sK1, sV1, j);
+        if (j + 1 < nkt) step(sK1, sV1, sK0, sV0, j + 1);
     }
+    wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it exits
 
     // Epilogue: O = acc / l, L = (m + log2 l) * ln 2 (natural log of the scaled scores).
 #pragma unroll
@@ -242,7 +250,7 @@ static int run_fwd(const void *q, const void *k, const void *v, void *o, float *
 template <typename T, int D>
 static int fwd_for(const void *q, const void *k, const void *v, void *o, float *lse, int BH, int S,
                    float scale, int causal, hipStream_t stream) {
-    return run_fwd<T, FwdTile<T, D, 1, 64>>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    return run_fwd<T, FwdTile<T, D, 1, 64, 4>>(q, k, v, o, lse, BH, S, scale, causal, stream);
 }
 
 template <typename T>
