@@ -68,10 +68,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const T *__restrict__ o, con
 
 // --------------------------------------------------------- key-outer dK/dV ---
 
-template <typename T, int D_, int BQ2_>
+template <typename T, int D_, int BQ2_, int NW_>
 struct KvTile {
     static constexpr int D = D_, BQ2 = BQ2_;
-    static constexpr int NW = 4, NT = NW * kWave;
+    static constexpr int NW = NW_, NT = NW * kWave;
     static constexpr int BKV = NW * 32;               // keys per workgroup
     static constexpr int NQ2 = BQ2 / 32;              // 32-query blocks per query tile
     static constexpr int KPL = Mma<T>::KPL;
@@ -80,7 +80,8 @@ struct KvTile {
     static constexpr int NI = 16 / KPL;
     using SW = Swz<T, D>;
     static constexpr int TILE = BQ2 * SW::PITCH;      // elements per Q or dO tile
-    static_assert(D % 16 == 0 && BQ2 % 32 == 0, "tile shape");
+    using DMA = TileDma<T, D, BQ2, NW>;
+    static_assert(D % 16 == 0 && BQ2 % 32 == 0 && BQ2 <= kWave, "tile shape");
 };
 
 template <typename T, typename C>
@@ -93,12 +94,15 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, BQ2 = C::BQ2;
-    __shared__ __attribute__((aligned(16))) T sQ[C::TILE];
-    __shared__ __attribute__((aligned(16))) T sdO[C::TILE];
-    __shared__ __attribute__((aligned(16))) float sL[BQ2];
-    __shared__ __attribute__((aligned(16))) float sDl[BQ2];
+    // Two stages of Q and dO tiles (each its own array, see the forward
+    // kernel) and of the tile's L and D values, one 64-entry copy per wave.
+    __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE];
+    __shared__ __attribute__((aligned(16))) float sL0[C::NW * kWave], sL1[C::NW * kWave];
+    __shared__ __attribute__((aligned(16))) float sD0[C::NW * kWave], sD1[C::NW * kWave];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
     const int kt = bid / BH;  // ascending: the tiles with the most query tiles go first
@@ -115,11 +119,6 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     const int k0 = kt * C::BKV;
     const int kw0 = k0 + wave * 32;
     const int key = kw0 + l32;  // this lane's key column
-
-    if constexpr (C::SW::CPR != C::SW::PCH) {
-        zero_lds<T, C::TILE, C::NT>(sQ, tid);
-        zero_lds<T, C::TILE, C::NT>(sdO, tid);
-    }
 
     // K^T and V^T fragments (B operands): lane owns key `key`, d-run of half h.
     frag kf[C::NSD], vf[C::NSD];
@@ -143,32 +142,28 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     const int nq2 = (S + BQ2 - 1) / BQ2;
     const int i0 = causal ? k0 / BQ2 : 0;
 
-    TileLoader<T, D, BQ2, C::NT> qio, dio;
-    float lreg = 0.f, dreg = 0.f;
-    auto prefetch = [&](int qt) {
-        qio.load(q, qt * BQ2, S, tid);
-        dio.load(dout, qt * BQ2, S, tid);
-        if (tid < BQ2) {
-            const int qi = qt * BQ2 + tid;
-            // rows past the end get L = +inf, so exp(S - L) = 0 there
-            lreg = qi < S ? lse[qi] * kLog2e : INFINITY;
-            dreg = qi < S ? delta[qi] : 0.f;
-        }
+    typename C::DMA dma;
+    dma.init(lane, wave);
+    typedef __attribute__((address_space(3))) void lds_void;
+    // Q, dO rows and their L, D values for query tile `it` (rows past the end
+    // load the last row; they are masked)
+    auto issue = [&](T *nQ, T *ndO, float *nL, float *nD, int it) {
+        dma.issue(nQ, q, it * BQ2, S, wave);
+        dma.issue(ndO, dout, it * BQ2, S, wave);
+        const int qi = min(it * BQ2 + lane, S - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(lse + qi), (lds_void *)(nL + wave * kWave), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(delta + qi), (lds_void *)(nD + wave * kWave), 4, 0, 0);
     };
-    if (i0 < nq2) prefetch(i0);
-    if constexpr (C::SW::CPR != C::SW::PCH) __syncthreads();
+    issue(sQ0, sdO0, sL0, sD0, i0);
 
-    for (int it = i0; it < nq2; ++it) {
+    auto step = [&](const T *tQ, const T *tdO, const float *tL, const float *tD, T *nQ, T *ndO,
+                    float *nL, float *nD, int it) {
         const int q0 = it * BQ2;
-        qio.store(sQ, tid);
-        dio.store(sdO, tid);
-        if (tid < BQ2) {
-            sL[tid] = lreg;
-            sDl[tid] = dreg;
-        }
-        __syncthreads();
-        if (it + 1 < nq2) prefetch(it + 1);
-
+        // prefetch query tile it+1 unconditionally (see the forward kernel)
+        issue(nQ, ndO, nL, nD, it + 1);
+        wait_vmcnt<2 * C::DMA::IPW + 2>();
+        lds_barrier();
+        const float *wL = tL + wave * kWave, *wD = tD + wave * kWave;
         const bool active = kw0 < S && !(causal && q0 + BQ2 - 1 < kw0);
         if (active) {
             const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
@@ -178,13 +173,13 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                 f32x16 s = f32x16{}, dp = f32x16{};
                 {
                     frag qa[C::NSD];
-                    load_row_frags<T, D>(qa, sQ, qb * 32 + sigma(l32), h);
+                    load_row_frags<T, D>(qa, tQ, qb * 32 + sigma(l32), h);
 #pragma unroll
                     for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], kf[st], s);
                 }
                 {
                     frag da[C::NSD];
-                    load_row_frags<T, D>(da, sdO, qb * 32 + sigma(l32), h);
+                    load_row_frags<T, D>(da, tdO, qb * 32 + sigma(l32), h);
 #pragma unroll
                     for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], vf[st], dp);
                 }
@@ -192,14 +187,14 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 #pragma unroll
                 for (int hr = 0; hr < 2; ++hr) {
                     const int base = qb * 32 + 16 * hr + 8 * h;
-                    const f32x4 l0 = *reinterpret_cast<const f32x4 *>(sL + base);
-                    const f32x4 l1 = *reinterpret_cast<const f32x4 *>(sL + base + 4);
-                    const f32x4 d0 = *reinterpret_cast<const f32x4 *>(sDl + base);
-                    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(sDl + base + 4);
+                    const f32x4 l0 = *reinterpret_cast<const f32x4 *>(wL + base);
+                    const f32x4 l1 = *reinterpret_cast<const f32x4 *>(wL + base + 4);
+                    const f32x4 d0 = *reinterpret_cast<const f32x4 *>(wD + base);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(wD + base + 4);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        lv[8 * hr + t] = l0[t];
-                        lv[8 * hr + 4 + t] = l1[t];
+                        lv[8 * hr + t] = l0[t] * kLog2e;
+                        lv[8 * hr + 4 + t] = l1[t] * kLog2e;
                         dl[8 * hr + t] = d0[t];
                         dl[8 * hr + 4 + t] = d1[t];
                     }
@@ -223,17 +218,23 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 #pragma unroll
                 for (int db = 0; db < C::ND; ++db) {
                     frag a[C::NI];
-                    tr.load(a, sdO, qb, db, lane);
+                    tr.load(a, tdO, qb, db, lane);
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) dV[db] = M::run(a[i], pf[i], dV[db]);  // Eq. 15
-                    tr.load(a, sQ, qb, db, lane);
+                    tr.load(a, tQ, qb, db, lane);
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) dK[db] = M::run(a[i], sf[i], dK[db]);  // Eq. 19
                 }
             }
         }
-        __syncthreads();
+        wait_lgkm0();
+        lds_barrier();
+    };
+    for (int it = i0; it < nq2; it += 2) {
+        step(sQ0, sdO0, sL0, sD0, sQ1, sdO1, sL1, sD1, it);
+        if (it + 1 < nq2) step(sQ1, sdO1, sL1, sD1, sQ0, sdO0, sL0, sD0, it + 1);
     }
+    wait_vmcnt<0>();
 
     if (key < S) {
 #pragma unroll
@@ -251,10 +252,10 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 
 // -------------------------------------------------------- query-outer dQ ---
 
-template <typename T, int D_, int NQB_, int BK_>
+template <typename T, int D_, int NQB_, int BK_, int NW_>
 struct QTile {
     static constexpr int D = D_, NQB = NQB_, BK = BK_;
-    static constexpr int NW = 4, NT = NW * kWave;
+    static constexpr int NW = NW_, NT = NW * kWave;
     static constexpr int BQ = NW * NQB * 32;
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;
@@ -263,6 +264,7 @@ struct QTile {
     static constexpr int NI = 16 / KPL;
     using SW = Swz<T, D>;
     static constexpr int TILE = BK * SW::PITCH;       // elements per K or V tile
+    using DMA = TileDma<T, D, BK, NW>;
     static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
 };
 
@@ -276,10 +278,12 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
-    __shared__ __attribute__((aligned(16))) T sK[C::TILE];
-    __shared__ __attribute__((aligned(16))) T sV[C::TILE];
+    // two stages of K and V tiles, each its own array (see the forward kernel)
+    __shared__ __attribute__((aligned(1024))) T sK0[C::TILE], sK1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sV0[C::TILE], sV1[C::TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
@@ -294,11 +298,6 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     delta += (size_t)bh * S;
     const int q0 = qt * C::BQ;
     const int qw0 = q0 + wave * NQB * 32;
-
-    if constexpr (C::SW::CPR != C::SW::PCH) {
-        zero_lds<T, C::TILE, C::NT>(sK, tid);
-        zero_lds<T, C::TILE, C::NT>(sV, tid);
-    }
 
     // Q^T, dO^T fragments (B operands) and the row statistics of this lane's query.
     frag qf[NQB][C::NSD], df[NQB][C::NSD];
@@ -331,28 +330,26 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     int nkt = (S + BK - 1) / BK;
     if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
 
-    TileLoader<T, D, BK, C::NT> kio, vio;
-    kio.load(k, 0, S, tid);
-    vio.load(v, 0, S, tid);
-    if constexpr (C::SW::CPR != C::SW::PCH) __syncthreads();
+    typename C::DMA dma;
+    dma.init(lane, wave);
+    dma.issue(sK0, k, 0, S, wave);
+    dma.issue(sV0, v, 0, S, wave);
 
-    for (int j = 0; j < nkt; ++j) {
+    auto step = [&](const T *tK, const T *tV, T *nK, T *nV, int j) {
         const int j0 = j * BK;
-        kio.store(sK, tid);
-        vio.store(sV, tid);
-        __syncthreads();
-        if (j + 1 < nkt) {
-            kio.load(k, j0 + BK, S, tid);
-            vio.load(v, j0 + BK, S, tid);
-        }
+        // prefetch tile j+1 unconditionally (see the forward kernel)
+        dma.issue(nK, k, j0 + BK, S, wave);
+        dma.issue(nV, v, j0 + BK, S, wave);
+        wait_vmcnt<2 * C::DMA::IPW>();
+        lds_barrier();
         const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
         if (active) {
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 frag ka[C::NSD], va[C::NSD];
-                load_row_frags<T, D>(ka, sK, kb * 32 + sigma(l32), h);
-                load_row_frags<T, D>(va, sV, kb * 32 + sigma(l32), h);
+                load_row_frags<T, D>(ka, tK, kb * 32 + sigma(l32), h);
+                load_row_frags<T, D>(va, tV, kb * 32 + sigma(l32), h);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     // S^T block: rows = keys j0 + 32*kb + idx_of(r, h), col = query.
@@ -374,15 +371,21 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
                     for (int db = 0; db < C::ND; ++db) {
                         frag a[C::NI];
-                        tr.load(a, sK, kb, db, lane);
+                        tr.load(a, tK, kb, db, lane);
 #pragma unroll
                         for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(a[i], sf[i], acc[qb][db]);  // Eq. 18
                     }
                 }
             }
         }
-        __syncthreads();
+        wait_lgkm0();
+        lds_barrier();
+    };
+    for (int j = 0; j < nkt; j += 2) {
+        step(sK0, sV0, sK1, sV1, j);
+        if (j + 1 < nkt) step(sK1, sV1, sK0, sV0, j + 1);
     }
+    wait_vmcnt<0>();
 
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -415,8 +418,8 @@ template <typename T, int D>
 static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                    const float *delta, void *dq, void *dk, void *dv, int BH, int S, float scale,
                    int causal, hipStream_t stream) {
-    using KC = KvTile<T, D, 64>;
-    using QC = QTile<T, D, 1, 64>;
+    using KC = KvTile<T, D, (sizeof(T) == 4 && D > 64) ? 32 : 64, 4>;
+    using QC = QTile<T, D, 1, 64, 4>;
     const float c = scale * kLog2e;
     const long long g1 = (long long)((S + KC::BKV - 1) / KC::BKV) * BH;
     const int nqt = (S + QC::BQ - 1) / QC::BQ;
