@@ -33,6 +33,22 @@ PEAK_BF16 = 2516.6   # TFLOP/s, dense bf16 matrix cores (256 CU x 4096 FLOP/clk 
 PEAK_F32 = 157.3     # TFLOP/s, dense fp32 matrix cores
 DEFAULT_WORKLOAD = "bf16_b1h16_s65536_d128"
 
+# HBM traffic of one forward-kernel launch on the default workload, from two
+# rocprofv3 --pmc passes (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a
+# plain 1 GiB copy calibrates; see profiles/), keyed by a hash of the forward
+# kernel's sources: once those change, the figure is stale and reported as null.
+FWD_TRAFFIC = {"sources_sha1": "d954c3322dcff0870f76756c9dd99e49de707b47", "bytes": 9437324672}
+FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp")
+
+
+def fwd_sources_sha1():
+    import hashlib
+    h = hashlib.sha1()
+    for f in FWD_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -180,7 +196,8 @@ def main():
         "ms": {"fwd": round(t_fwd, 4), "bwd_preprocess": round(t_pre, 4), "bwd": round(t_bwd, 4)},
         "roofline": {"kernel": "fwd_kernel (fa_fwd)", "bound": "mfma", "achieved": round(fwd_tf, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tf / peak, 4),
-                     "traffic": None,
+                     "traffic": (FWD_TRAFFIC["bytes"] if w.name == DEFAULT_WORKLOAD
+                                 and FWD_TRAFFIC["sources_sha1"] == fwd_sources_sha1() else None),
                      "algorithmic_per_launch": {"flop": f_fwd, "bytes": 4 * tensor + 4 * B * H * S}},
         "roofline_bwd": {"kernel": "dkdv_kernel + dq_kernel (fa_bwd)", "bound": "mfma",
                          "achieved": round(bwd_tf, 2), "peak": peak, "unit": "TFLOP/s",
