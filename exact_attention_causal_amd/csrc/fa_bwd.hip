@@ -78,9 +78,8 @@ struct KvTile {
     static constexpr int NSD = D / 2 / KPL;
     static constexpr int ND = (D + 31) / 32;
     static constexpr int NI = 16 / KPL;
-    using SW = Swz<T, D>;
-    static constexpr int TILE = BQ2 * SW::PITCH;      // elements per Q or dO tile
     using DMA = TileDma<T, D, BQ2, NW>;
+    static constexpr int TILE = DMA::ELEMS;           // elements per Q or dO tile
     static_assert(D % 16 == 0 && BQ2 % 32 == 0 && BQ2 <= kWave, "tile shape");
 };
 
@@ -150,7 +149,12 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     auto issue = [&](T *nQ, T *ndO, float *nL, float *nD, int it) {
         dma.issue(nQ, q, it * BQ2, S, wave);
         dma.issue(ndO, dout, it * BQ2, S, wave);
-        const int qi = min(it * BQ2 + lane, S - 1);
+        // slot j holds the query whose L and D lane half h reads as registers
+        // 8u..8u+7 of its 32-query block: slot 16u + 8h + 4rr + e <-> query
+        // ridx(8u + 4rr + e, h), so each half reads two runs of 8 slots
+        const int jq = 32 * (lane >> 5) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3) +
+                       2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
+        const int qi = min(it * BQ2 + jq, S - 1);
         __builtin_amdgcn_global_load_lds((const void *)(lse + qi), (lds_void *)(nL + wave * kWave), 4, 0, 0);
         __builtin_amdgcn_global_load_lds((const void *)(delta + qi), (lds_void *)(nD + wave * kWave), 4, 0, 0);
     };
@@ -169,17 +173,17 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
             const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
 #pragma unroll
             for (int qb = 0; qb < C::NQ2; ++qb) {
-                // S block: rows = queries q0 + 32*qb + idx_of(r, h), col = key.
+                // S block: rows = queries q0 + 32*qb + ridx(r, h), col = key.
                 f32x16 s = f32x16{}, dp = f32x16{};
                 {
                     frag qa[C::NSD];
-                    load_row_frags<T, D>(qa, tQ, qb * 32 + sigma(l32), h);
+                    load_row_frags<T, D>(qa, tQ, qb * 32 + rsigma(l32), h);
 #pragma unroll
                     for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], kf[st], s);
                 }
                 {
                     frag da[C::NSD];
-                    load_row_frags<T, D>(da, tdO, qb * 32 + sigma(l32), h);
+                    load_row_frags<T, D>(da, tdO, qb * 32 + rsigma(l32), h);
 #pragma unroll
                     for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], vf[st], dp);
                 }
@@ -199,14 +203,14 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                         dl[8 * hr + 4 + t] = d1[t];
                     }
                 }
-                // query q0 + 32*qb + idx_of(r, h) is kept iff it is at least `lo` and below `hi`
-                const int lo = (causal ? key : 0) - q0 - 32 * qb - 8 * h;
-                const int hi = S - q0 - 32 * qb - 8 * h;
+                // query q0 + 32*qb + ridx(r, h) is kept iff it is at least `lo` and below `hi`
+                const int lo = (causal ? key : 0) - q0 - 32 * qb - 2 * h;
+                const int hi = S - q0 - 32 * qb - 2 * h;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float p = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
                     if (need_mask) {
-                        const int e = 16 * (r / 8) + (r % 8);
+                        const int e = ridx(r, 0);
                         p = (e >= lo && e < hi) ? p : 0.f;
                     }
                     s[r] = p;
@@ -218,10 +222,10 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 #pragma unroll
                 for (int db = 0; db < C::ND; ++db) {
                     frag a[C::NI];
-                    tr.load(a, tdO, qb, db, lane);
+                    tr.load(a, tdO, qb, db);
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) dV[db] = M::run(a[i], pf[i], dV[db]);  // Eq. 15
-                    tr.load(a, tQ, qb, db, lane);
+                    tr.load(a, tQ, qb, db);
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) dK[db] = M::run(a[i], sf[i], dK[db]);  // Eq. 19
                 }
@@ -262,9 +266,8 @@ struct QTile {
     static constexpr int NKB = BK / 32;
     static constexpr int ND = (D + 31) / 32;
     static constexpr int NI = 16 / KPL;
-    using SW = Swz<T, D>;
-    static constexpr int TILE = BK * SW::PITCH;       // elements per K or V tile
     using DMA = TileDma<T, D, BK, NW>;
+    static constexpr int TILE = DMA::ELEMS;           // elements per K or V tile
     static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
 };
 
@@ -347,23 +350,32 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
-                frag ka[C::NSD], va[C::NSD];
-                load_row_frags<T, D>(ka, tK, kb * 32 + sigma(l32), h);
-                load_row_frags<T, D>(va, tV, kb * 32 + sigma(l32), h);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
-                    // S^T block: rows = keys j0 + 32*kb + idx_of(r, h), col = query.
+                    // S^T block: rows = keys j0 + 32*kb + ridx(r, h), col = query.
+                    // (K and V fragments are not live at the same time: keeps two
+                    // waves' worth of registers per SIMD)
                     f32x16 s = f32x16{}, dp = f32x16{};
+                    {
+                        frag ka[C::NSD];
+                        load_row_frags<T, D>(ka, tK, kb * 32 + rsigma(l32), h);
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) s = M::run(ka[st], qf[qb][st], s);
+                        for (int st = 0; st < C::NSD; ++st) s = M::run(ka[st], qf[qb][st], s);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    {
+                        frag va[C::NSD];
+                        load_row_frags<T, D>(va, tV, kb * 32 + rsigma(l32), h);
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) dp = M::run(va[st], df[qb][st], dp);
+                        for (int st = 0; st < C::NSD; ++st) dp = M::run(va[st], df[qb][st], dp);
+                    }
                     const int qi = qw0 + qb * 32 + l32;
-                    const int t = (causal ? min(qi + 1, S) : S) - j0 - 32 * kb - 8 * h;
+                    const int t = (causal ? min(qi + 1, S) : S) - j0 - 32 * kb - 2 * h;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float p = fast_exp2(fmaf(s[r], c, -lq[qb]));  // Eq. 14
-                        if (need_mask) p = (16 * (r / 8) + (r % 8) < t) ? p : 0.f;
+                        if (need_mask) p = (ridx(r, 0) < t) ? p : 0.f;
                         dp[r] = p * (dp[r] - dl[qb]);  // Eq. 17
                     }
                     frag sf[C::NI];
@@ -371,7 +383,7 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
                     for (int db = 0; db < C::ND; ++db) {
                         frag a[C::NI];
-                        tr.load(a, tK, kb, db, lane);
+                        tr.load(a, tK, kb, db);
 #pragma unroll
                         for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(a[i], sf[i], acc[qb][db]);  // Eq. 18
                     }

@@ -9,17 +9,21 @@
 //     instruction; fp32 (v_mfma_f32_32x32x2f32): one k-slot per lane.
 //
 // Because a reduction does not care in which order its terms are summed, the
-// kernels choose the mapping from MFMA rows and k-slots to real indices:
-//   * A-operand row rho of a 32-row block is the real index sigma(rho), chosen
-//     so that output register r of half h belongs to index
-//         idx(r, h) = 16*(r/8) + 8*h + r%8,
-//     i.e. registers 0..7 of a half are 8 consecutive indices and 8..15 the
-//     next 8 + 8.  An output block can therefore be fed straight back as the
-//     B operand of the next product (k-slots of instruction u = registers
-//     u*KPL ..), and the matching A operand is two runs of 8 consecutive
-//     elements per lane -- one 16-byte LDS read each for bf16.
-//   * For products reducing over the head dimension, half h of the lanes owns
-//     d in [h*D/2, (h+1)*D/2); instruction s takes KPL consecutive d of it.
+// kernels choose which real index each A-operand row and each k-slot stands
+// for.  Two mappings are used:
+//   * reduction rows (keys in the forward and dQ passes, queries in the dK/dV
+//     pass): output register r of half h is index
+//         ridx(r, h) = 16*(r/8) + 4*(r%4) + 2*h + (r/4)%2.
+//     An output block is then the B operand of the next product as it stands
+//     (instruction u takes registers 8u..8u+7), and the matching A operand --
+//     read with the LDS transpose instruction -- takes every 4th row of the
+//     tile, which with a padded row pitch keeps LDS banks conflict-free;
+//   * head-dimension rows of the outputs: register r of half h is
+//         didx(r, h) = 16*(r/8) + 8*h + r%8,
+//     so registers 0..7 and 8..15 of a lane are runs of 8 consecutive d and
+//     the epilogue stores 16 bytes at a time.
+// For products reducing over the head dimension, half h of the lanes owns d
+// in [h*D/2, (h+1)*D/2); instruction s takes KPL consecutive d of it.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,12 +62,19 @@ template <> struct Mma<float> {
     __device__ static inline frag zero() { return 0.f; }
 };
 
-// Real index of output register r for lane half h (see header).
-__device__ __host__ constexpr inline int idx_of(int r, int h) { return 16 * (r / 8) + 8 * h + (r % 8); }
-
-// Real index that A-operand row rho stands for, so that output rows line up with idx_of.
-__device__ __host__ constexpr inline int sigma(int rho) {
-    return idx_of(4 * (rho / 8) + (rho % 4), (rho / 4) % 2);
+// Reduction-row index of output register r of half h (see header).
+__device__ __host__ constexpr inline int ridx(int r, int h) {
+    return 16 * (r / 8) + 4 * (r % 4) + 2 * h + (r / 4) % 2;
+}
+// Reduction-row index that A-operand row rho stands for (so output rows line up with ridx).
+__device__ __host__ constexpr inline int rsigma(int rho) {
+    return 16 * (rho / 16) + 4 * (rho % 4) + 2 * ((rho / 4) % 2) + (rho / 8) % 2;
+}
+// Head-dimension index of output register r of half h.
+__device__ __host__ constexpr inline int didx(int r, int h) { return 16 * (r / 8) + 8 * h + (r % 8); }
+// Head-dimension index that A-operand row rho stands for.
+__device__ __host__ constexpr inline int dsigma(int rho) {
+    return 16 * (rho / 16) + 8 * ((rho / 4) % 2) + 4 * ((rho / 8) % 2) + rho % 4;
 }
 
 // ---- fragments ------------------------------------------------------------
@@ -111,81 +122,44 @@ __device__ inline void to_bfrag(typename Mma<T>::frag (&dst)[16 / Mma<T>::KPL], 
     }
 }
 
-// ---- swizzled row-major LDS tiles -----------------------------------------
+// ---- padded row-major LDS tiles --------------------------------------------
 //
-// Every LDS tile is row-major with a power-of-two pitch of 8, 16 or 32
-// 16-byte chunks per row, and logical chunk c of row r sits at physical chunk
-// c ^ f(r).  f is chosen so that both read patterns the kernels use are free
-// of bank conflicts on the 64 four-byte LDS banks:
-//   * "row" reads (A operand reducing over columns): 16 lanes read one
-//     16-byte chunk each from 16 different rows;
-//   * "transposed" reads (ds_read_b64_tr_b16, A operand reducing over rows):
-//     32 lanes read 4 consecutive rows x 64 bytes.
-// Chunks at or beyond the logical row length stay zero (the tile is cleared
-// once), which is how head dimensions pad to whole 32-row output blocks.
+// Every LDS tile is row-major with a row pitch of D + 16 bytes' worth of
+// elements, i.e. 4 (mod 8) four-byte words for every head dimension used.  On
+// the 64 four-byte LDS banks that makes both read patterns conflict-free:
+//   * row reads (A operand reducing over the head dimension): 16 lanes read
+//     one 16-byte chunk each from 16 consecutive rows -> 16 distinct 4-bank
+//     groups;
+//   * transposed reads (ds_read_b64_tr_b16, A operand reducing over rows):
+//     32 lanes read 4 rows spaced 4 apart x 64 bytes -> 4 disjoint 16-bank
+//     windows.
+// Every per-lane address is then one base register plus an immediate offset.
 
 template <typename T, int D>
-struct Swz {
-    static constexpr int CW = 16 / sizeof(T);                            // elements per chunk
-    static constexpr int CPR = D / CW;                                   // logical chunks per row
-    static constexpr int PCH = CPR <= 8 ? 8 : (CPR <= 16 ? 16 : 32);     // physical chunks per row
-    static constexpr int PITCH = PCH * CW;                               // elements per row
+struct Pad {
+    static constexpr int CW = 16 / sizeof(T);          // elements per 16-byte chunk
+    static constexpr int CPR = D / CW;                 // data chunks per row
+    static constexpr int SLOTS = CPR + 1;              // 16-byte slots per row (one pad)
+    static constexpr int PITCH = SLOTS * CW;           // elements per row
     static_assert(D % CW == 0, "rows must be whole 16-byte chunks");
-    __device__ static constexpr inline int f(int r) {
-        return PCH == 8 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : 4 * (r & 3) + ((r >> 2) & 3);
-    }
-    // element offset of logical chunk c of row r
-    __device__ static constexpr inline int off(int r, int c) { return r * PITCH + ((c ^ f(r)) * CW); }
-    // element offset of column `col` of row r
-    __device__ static constexpr inline int at(int r, int col) { return off(r, col / CW) + col % CW; }
-};
-
-// Global -> registers -> LDS mover for an R-row tile of a [S][D] head.
-// Unit u is chunk u % CPR of row u / CPR, so consecutive threads read
-// consecutive 16-byte chunks.  Rows at or beyond S read as zero.
-template <typename T, int D, int R, int NT>
-struct TileLoader {
-    using SW = Swz<T, D>;
-    static constexpr int UNITS = R * SW::CPR;
-    static constexpr int UPT = (UNITS + NT - 1) / NT;
-    u32x4 reg[UPT];
-
-    __device__ inline void load(const T *base, int row0, int S, int tid) {
-#pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-            const int u = tid + i * NT;
-            const int r = u / SW::CPR, c = u % SW::CPR;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if ((UNITS % NT == 0 || u < UNITS) && row0 + r < S)
-                x = *reinterpret_cast<const u32x4 *>(base + (size_t)(row0 + r) * D + c * SW::CW);
-            reg[i] = x;
-        }
-    }
-    __device__ inline void store(T *lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-            const int u = tid + i * NT;
-            if (UNITS % NT != 0 && u >= UNITS) continue;
-            const int r = u / SW::CPR, c = u % SW::CPR;
-            *reinterpret_cast<u32x4 *>(lds + SW::off(r, c)) = reg[i];
-        }
-    }
+    static_assert(((PITCH * sizeof(T) / 4) % 8) == 4, "pitch must be 4 (mod 8) words");
 };
 
 // Direct global -> LDS tile loads (global_load_lds_dwordx4): each instruction
 // of a wave writes 1 KiB of consecutive LDS (16 bytes per lane, in lane
-// order), so a lane is told which global chunk belongs at its LDS position of
-// the swizzled tile.  Rows past the end of the sequence load the last row and
-// padding chunks load the row's last chunk: the values are finite, and the
-// kernels mask those rows or never store the outputs they feed.
+// order), so each lane fetches the global chunk that belongs at its LDS slot.
+// The tile's slots are rounded up to whole instructions for every wave; slots
+// past the last row, pad slots and rows past the end of the sequence all fetch
+// a valid (clamped) chunk: the values are finite, and the kernels mask those
+// rows or never use what lands in the pad.
 template <typename T, int D, int R, int NW>
 struct TileDma {
-    using SW = Swz<T, D>;
-    static constexpr int ROW_BYTES = SW::PITCH * (int)sizeof(T);
-    static constexpr int RPI = 1024 / ROW_BYTES;      // rows per instruction
-    static constexpr int NINS = R / RPI;              // instructions per tile
-    static constexpr int IPW = NINS / NW;             // instructions per wave
-    static_assert(1024 % ROW_BYTES == 0 && R % RPI == 0 && NINS % NW == 0, "tile/DMA shape");
+    using PD = Pad<T, D>;
+    static constexpr int NSLOT = R * PD::SLOTS;
+    static constexpr int IPW = (NSLOT + 64 * NW - 1) / (64 * NW);  // instructions per wave
+    static constexpr int ELEMS = IPW * NW * 64 * PD::CW;          // tile allocation (elements)
+    // transposed reads of the last 32-column block may run up to 32 elements past a row
+    static_assert(R * PD::PITCH + 32 <= ELEMS || PD::CPR * PD::CW % 32 == 0, "tile slack");
     int row[IPW];  // row within the tile
     int col[IPW];  // element column of the chunk
 
@@ -193,10 +167,8 @@ struct TileDma {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int p = (wave * IPW + i) * 64 + lane;  // 16-byte slot within the tile
-            const int r = p / SW::PCH, pc = p % SW::PCH;
-            const int c = min(pc ^ SW::f(r), SW::CPR - 1);
-            row[i] = r;
-            col[i] = c * SW::CW;
+            row[i] = min(p / PD::SLOTS, R - 1);
+            col[i] = min(p % PD::SLOTS, PD::CPR - 1) * PD::CW;
         }
     }
     // Issue this wave's share of the tile holding rows row0 .. row0 + R - 1.
@@ -230,83 +202,52 @@ __device__ inline void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Clear n elements of LDS (n a multiple of 8 bytes' worth is not required; 16-byte steps).
-template <typename T, int N, int NT>
-__device__ inline void zero_lds(T *lds, int tid) {
-    static_assert((N * sizeof(T)) % 16 == 0, "tile bytes must be a multiple of 16");
-    constexpr int CH = N * sizeof(T) / 16;
-    for (int u = tid; u < CH; u += NT) reinterpret_cast<u32x4 *>(lds)[u] = u32x4{0u, 0u, 0u, 0u};
-}
-
-// A-operand fragments reducing over the head dimension, from rows of a tile:
-// lane (h, l32) takes row `row` and columns [h*D/2, (h+1)*D/2) (D/2/KPL fragments).
+// A-operand fragments reducing over the head dimension, from row `row` of a
+// tile: lane half h takes columns [h*D/2, (h+1)*D/2) (D/2/KPL fragments).
 template <typename T, int D>
 __device__ inline void load_row_frags(typename Mma<T>::frag (&dst)[D / 2 / Mma<T>::KPL], const T *tile,
                                       int row, int h) {
-    using SW = Swz<T, D>;
-    constexpr int KPL = Mma<T>::KPL;
-    constexpr int NCH = D / 2 / SW::CW;  // chunks per half row
-    const T *rp = tile + row * SW::PITCH;
-    const int fx = SW::f(row);
-#pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(rp + (((h * NCH + q) ^ fx) * SW::CW));
-        if constexpr (KPL == 8) {
-            dst[q] = __builtin_bit_cast(bf16x8, x);
-        } else {
-            const f32x4 v = __builtin_bit_cast(f32x4, x);
-            dst[4 * q + 0] = v[0];
-            dst[4 * q + 1] = v[1];
-            dst[4 * q + 2] = v[2];
-            dst[4 * q + 3] = v[3];
-        }
-    }
+    load_run<T, D / 2 / Mma<T>::KPL>(dst, tile + row * Pad<T, D>::PITCH + h * (D / 2));
 }
 
-// A-operand fragments reducing over 32 rows of a tile (rows 32*kb + idx_of(r, h)),
-// output row = column 32*cb + sigma(l32).  bf16 uses the LDS transpose read
+// A-operand fragments reducing over 32 rows of a tile (rows 32*kb + ridx(r, h)),
+// output row = column 32*cb + dsigma(l32).  bf16 uses the LDS transpose read
 // ds_read_b64_tr_b16: in each 16-lane group, destination lane i receives
-// column i of the 4 x 16 block whose row k, columns 4c..4c+3 the source lane
-// 4k + c points at.  fp32 reads single elements.
+// column i of the 4 x 16 block whose row e, columns 4c..4c+3 source lane
+// 4e + c points at.  fp32 reads single elements.
 template <typename T, int D>
 struct TransReader {
-    using SW = Swz<T, D>;
-    static constexpr int NCB = (D + 31) / 32;  // 32-column output blocks
+    using PD = Pad<T, D>;
     static constexpr int NI = 16 / Mma<T>::KPL;
-    int off[NCB][2];  // bf16: per output block and half-fragment, lane offset within a 16-row slab
+    int base;  // per-lane element offset; everything else is an immediate
 
     __device__ inline void init(int lane) {
+        const int h = lane >> 5;
         if constexpr (Mma<T>::KPL == 8) {
-            const int g = lane >> 4, j = lane & 15, k = j >> 2, c = j & 3;
-            const int h = g >> 1, sub = g & 1;
-            constexpr int perm4[4] = {0, 8, 4, 12};
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const int row = 4 * rr + 8 * h + k;          // row within a 16-row slab
-                    const int col = 32 * cb + 16 * sub + perm4[c];
-                    off[cb][rr] = SW::at(row, col);
-                }
+            const int g = lane >> 4, j = lane & 15, e = j >> 2, c = j & 3;
+            const int sub = g & 1;
+            // source row 4e + 2h (+1 for the second read) of a 16-row slab;
+            // the four 4-column chunks of a group cover dsigma of its 16 lanes
+            base = (4 * e + 2 * h) * PD::PITCH + 16 * sub + 4 * ((c & 1) * 2 + (c >> 1));
+        } else {
+            base = 2 * h * PD::PITCH + dsigma(lane & 31);
         }
     }
 
-    __device__ inline void load(typename Mma<T>::frag (&dst)[NI], const T *tile, int kb, int cb, int lane) const {
+    __device__ inline void load(typename Mma<T>::frag (&dst)[NI], const T *tile, int kb, int cb) const {
         if constexpr (Mma<T>::KPL == 8) {
+            typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const T *slab = tile + (32 * kb + 16 * u) * SW::PITCH;  // rows 32kb+16u .. +15
-                typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-                const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4 *)(slab + off[cb][0]));
-                const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4 *)(slab + off[cb][1]));
+                const T *p = tile + base + (32 * kb + 16 * u) * PD::PITCH + 32 * cb;
+                const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+                const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + PD::PITCH));
                 dst[u] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
             }
         } else {
-            const int h = lane >> 5, col = 32 * cb + sigma(lane & 31);
+            const T *p = tile + base + 32 * kb * PD::PITCH + 32 * cb;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dst[r] = tile[SW::at(32 * kb + idx_of(r, h), col)];
+            for (int r = 0; r < 16; ++r) dst[r] = p[ridx(r, 0) * PD::PITCH];
         }
     }
 };

@@ -19,7 +19,7 @@
 //   * exponentials are exp2 with scale*log2(e) folded into one FMA, and the
 //     stored L is converted back to the natural-log convention (lecture notes
 //     "A2 系统" at courses-9tz.pages.dev/llm/systems, section "从公式到 Triton 程序");
-//   * K and V tiles sit row-major in LDS with an XOR swizzle; V^T operand
+//   * K and V tiles sit row-major in LDS with a padded pitch; V^T operand
 //     fragments come straight from the row-major tile through the gfx950
 //     transposing LDS read, so nothing is transposed on the way in;
 //   * the accumulator is rescaled only when a new score exceeds the running
@@ -44,9 +44,8 @@ struct FwdTile {
     static constexpr int NKB = BK / 32;               // 32-key blocks per tile
     static constexpr int ND = (D + 31) / 32;          // 32-row output blocks over d
     static constexpr int NI = 16 / KPL;               // MFMAs per 32-key reduction block
-    using SW = Swz<T, D>;
-    static constexpr int TILE = BK * SW::PITCH;       // elements per K or V tile
     using DMA = TileDma<T, D, BK, NW>;
+    static constexpr int TILE = DMA::ELEMS;           // elements per K or V tile
     static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
 };
 
@@ -129,12 +128,12 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
         lds_barrier();                  // every wave's part of tile j has landed
         const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
         if (active) {
-            // S^T block (kb, qb): rows = keys j0 + 32*kb + idx_of(r, h), col = query.
+            // S^T block (kb, qb): rows = keys j0 + 32*kb + ridx(r, h), col = query.
             f32x16 s[NQB][C::NKB];
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 frag kf[C::NSD];
-                load_row_frags<T, D>(kf, tK, kb * 32 + sigma(l32), h);
+                load_row_frags<T, D>(kf, tK, kb * 32 + rsigma(l32), h);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     f32x16 t = f32x16{};
@@ -145,17 +144,17 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
             }
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
             if (need_mask) {
-                // key j0 + 32*kb + idx_of(r, h) is kept iff it is below `lim`
+                // key j0 + 32*kb + ridx(r, h) is kept iff it is below `lim`
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     const int qi = qw0 + qb * 32 + l32;
                     const int lim = causal ? min(qi + 1, S) : S;
-                    const int t = lim - j0 - 8 * h;
+                    const int t = lim - j0 - 2 * h;
 #pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            s[qb][kb][r] = (32 * kb + 16 * (r / 8) + (r % 8) < t) ? s[qb][kb][r] : -INFINITY;
+                            s[qb][kb][r] = (32 * kb + ridx(r, 0) < t) ? s[qb][kb][r] : -INFINITY;
                 }
             }
             // Online softmax in base 2 (scores scaled by c = scale*log2 e).  The
@@ -199,7 +198,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
 #pragma unroll
                 for (int db = 0; db < C::ND; ++db) {
                     frag vf[C::NI];
-                    vt.load(vf, tV, kb, db, lane);
+                    vt.load(vf, tV, kb, db);
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
