@@ -67,19 +67,31 @@ __global__ __launch_bounds__(256) void delta_kernel(const T *__restrict__ o, con
 }
 
 // --------------------------------------------------------- key-outer dK/dV ---
+//
+// Each 32-key block is owned by a pair of waves that split the block's four
+// products between them (no product is computed twice):
+//   * the P wave forms S = Q K^T, P = exp(S - L) (Eq. 13-14), hands P to its
+//     partner through LDS and accumulates dV^T += dO^T P (Eq. 15);
+//   * the dS wave forms dP = dO V^T (Eq. 16) while its partner works on P,
+//     then dS = P o (dP - D) (Eq. 17) and accumulates dK^T += Q^T dS (Eq. 19).
+// So each wave keeps one B operand (K^T or V^T) and one accumulator in
+// registers, which leaves room for two waves per SIMD.
 
-template <typename T, int D_, int BQ2_, int NW_>
+template <typename T, int D_, int BQ2_>
 struct KvTile {
     static constexpr int D = D_, BQ2 = BQ2_;
-    static constexpr int NW = NW_, NT = NW * kWave;
-    static constexpr int BKV = NW * 32;               // keys per workgroup
+    static constexpr int NW = 8, NT = NW * kWave;
+    static constexpr int NPAIR = NW / 2;
+    static constexpr int BKV = NPAIR * 32;            // keys per workgroup
     static constexpr int NQ2 = BQ2 / 32;              // 32-query blocks per query tile
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;
     static constexpr int ND = (D + 31) / 32;
     static constexpr int NI = 16 / KPL;
-    using DMA = TileDma<T, D, BQ2, NW>;
+    using DMA = TileDma<T, D, BQ2, NW / 2>;           // the P waves load Q, the dS waves dO
+    using PD = typename DMA::PD;
     static constexpr int TILE = DMA::ELEMS;           // elements per Q or dO tile
+    static constexpr int PBLK = 64 * 16;              // P values of one 32x32 block (elements)
     static_assert(D % 16 == 0 && BQ2 % 32 == 0 && BQ2 <= kWave, "tile shape");
 };
 
@@ -94,14 +106,17 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     using frag = typename M::frag;
     constexpr int D = C::D, BQ2 = C::BQ2;
     // Two stages of Q and dO tiles (each its own array, see the forward
-    // kernel) and of the tile's L and D values, one 64-entry copy per wave.
+    // kernel) and of the tile's L (P waves) or D (dS waves) values, one
+    // 64-entry copy per wave; plus the P hand-over buffer.
     __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE];
     __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE];
-    __shared__ __attribute__((aligned(16))) float sL0[C::NW * kWave], sL1[C::NW * kWave];
-    __shared__ __attribute__((aligned(16))) float sD0[C::NW * kWave], sD1[C::NW * kWave];
+    __shared__ __attribute__((aligned(16))) float sX0[C::NW * kWave], sX1[C::NW * kWave];
+    __shared__ __attribute__((aligned(16))) T sP[C::NPAIR * C::NQ2 * C::PBLK];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int role = wave / C::NPAIR;   // 0: P / dV wave, 1: dS / dK wave
+    const int pair = wave % C::NPAIR;
     const int h = lane >> 5, l32 = lane & 31;
     const int bid = blockIdx.x;
     const int kt = bid / BH;  // ascending: the tiles with the most query tiles go first
@@ -116,140 +131,175 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     lse += (size_t)bh * S;
     delta += (size_t)bh * S;
     const int k0 = kt * C::BKV;
-    const int kw0 = k0 + wave * 32;
+    const int kw0 = k0 + pair * 32;
     const int key = kw0 + l32;  // this lane's key column
 
-    // K^T and V^T fragments (B operands): lane owns key `key`, d-run of half h.
-    frag kf[C::NSD], vf[C::NSD];
-    if (key < S) {
-        load_run<T, C::NSD>(kf, k + (size_t)key * D + h * (D / 2));
-        load_run<T, C::NSD>(vf, v + (size_t)key * D + h * (D / 2));
-    } else {
-        zero_run<T, C::NSD>(kf);
-        zero_run<T, C::NSD>(vf);
-    }
+    // B operand of this wave's first product: K^T (P wave) or V^T (dS wave);
+    // lane owns key `key`, d-run of half h.
+    frag bf[C::NSD];
+    if (key < S)
+        load_run<T, C::NSD>(bf, (role ? v : k) + (size_t)key * D + h * (D / 2));
+    else
+        zero_run<T, C::NSD>(bf);
     TransReader<T, D> tr;
     tr.init(lane);
 
-    f32x16 dK[C::ND], dV[C::ND];
+    f32x16 acc[C::ND];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-    for (int db = 0; db < C::ND; ++db) {
-        dK[db] = f32x16{};
-        dV[db] = f32x16{};
-    }
+    for (int db = 0; db < C::ND; ++db) acc[db] = f32x16{};
 
     const int nq2 = (S + BQ2 - 1) / BQ2;
     const int i0 = causal ? k0 / BQ2 : 0;
 
     typename C::DMA dma;
-    dma.init(lane, wave);
+    dma.init(lane, pair);
     typedef __attribute__((address_space(3))) void lds_void;
-    // Q, dO rows and their L, D values for query tile `it` (rows past the end
-    // load the last row; they are masked)
-    auto issue = [&](T *nQ, T *ndO, float *nL, float *nD, int it) {
-        dma.issue(nQ, q, it * BQ2, S, wave);
-        dma.issue(ndO, dout, it * BQ2, S, wave);
-        // slot j holds the query whose L and D lane half h reads as registers
-        // 8u..8u+7 of its 32-query block: slot 16u + 8h + 4rr + e <-> query
-        // ridx(8u + 4rr + e, h), so each half reads two runs of 8 slots
+    // Q (P waves) or dO (dS waves) rows, and L (P waves) or D (dS waves) of
+    // query tile `it` (rows past the end load the last row; they are masked)
+    auto issue = [&](T *nQ, T *ndO, float *nX, int it) {
+        dma.issue(role ? ndO : nQ, role ? dout : q, it * BQ2, S, pair);
+        // slot j holds the query a lane half reads as registers 8u..8u+7 of its
+        // 32-query block: slot 16u + 8h + 4rr + e <-> query ridx(8u + 4rr + e, h),
+        // so each half reads two runs of 8 slots
         const int jq = 32 * (lane >> 5) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3) +
                        2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
         const int qi = min(it * BQ2 + jq, S - 1);
-        __builtin_amdgcn_global_load_lds((const void *)(lse + qi), (lds_void *)(nL + wave * kWave), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(delta + qi), (lds_void *)(nD + wave * kWave), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)((role ? delta : lse) + qi),
+                                         (lds_void *)(nX + wave * kWave), 4, 0, 0);
     };
-    issue(sQ0, sdO0, sL0, sD0, i0);
+    issue(sQ0, sdO0, sX0, i0);
 
-    auto step = [&](const T *tQ, const T *tdO, const float *tL, const float *tD, T *nQ, T *ndO,
-                    float *nL, float *nD, int it) {
+    auto step = [&](const T *tQ, const T *tdO, const float *tX, T *nQ, T *ndO, float *nX, int it) {
         const int q0 = it * BQ2;
         // prefetch query tile it+1 unconditionally (see the forward kernel)
-        issue(nQ, ndO, nL, nD, it + 1);
-        wait_vmcnt<2 * C::DMA::IPW + 2>();
+        issue(nQ, ndO, nX, it + 1);
+        wait_vmcnt<C::DMA::IPW + 1>();
         lds_barrier();
-        const float *wL = tL + wave * kWave, *wD = tD + wave * kWave;
+        const float *wX = tX + wave * kWave;
         const bool active = kw0 < S && !(causal && q0 + BQ2 - 1 < kw0);
-        if (active) {
-            const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
+        const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
+        // this wave's per-query statistic for registers r of block qb
+        auto stat = [&](float (&x)[16], int qb, float mul) {
 #pragma unroll
-            for (int qb = 0; qb < C::NQ2; ++qb) {
-                // S block: rows = queries q0 + 32*qb + ridx(r, h), col = key.
-                f32x16 s = f32x16{}, dp = f32x16{};
-                {
-                    frag qa[C::NSD];
-                    load_row_frags<T, D>(qa, tQ, qb * 32 + rsigma(l32), h);
+            for (int hr = 0; hr < 2; ++hr) {
+                const int base = qb * 32 + 16 * hr + 8 * h;
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(wX + base);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(wX + base + 4);
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], kf[st], s);
+                for (int t = 0; t < 4; ++t) {
+                    x[8 * hr + t] = a[t] * mul;
+                    x[8 * hr + 4 + t] = b[t] * mul;
                 }
-                {
+            }
+        };
+        T *pbuf = sP + pair * C::NQ2 * C::PBLK + lane * 16;
+        f32x16 dp[C::NQ2];
+        frag pf[C::NQ2][C::NI];
+        if (active) {
+            if (role == 0) {
+#pragma unroll
+                for (int qb = 0; qb < C::NQ2; ++qb) {
+                    // S block: rows = queries q0 + 32*qb + ridx(r, h), col = key.
+                    f32x16 s = f32x16{};
+                    {
+                        frag qa[C::NSD];
+                        load_row_frags<T, D>(qa, tQ, qb * 32 + rsigma(l32), h);
+#pragma unroll
+                        for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], bf[st], s);
+                    }
+                    float lv[16];
+                    stat(lv, qb, kLog2e);
+                    // query q0 + 32*qb + ridx(r, h) is kept iff it is at least `lo` and below `hi`
+                    const int lo = (causal ? key : 0) - q0 - 32 * qb - 2 * h;
+                    const int hi = S - q0 - 32 * qb - 2 * h;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
+                        if (need_mask) {
+                            const int e = ridx(r, 0);
+                            p = (e >= lo && e < hi) ? p : 0.f;
+                        }
+                        s[r] = p;
+                    }
+                    to_bfrag<T>(pf[qb], s);
+                    // hand P to the partner (same lane layout on both sides)
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i)
+                        *reinterpret_cast<typename M::frag *>(pbuf + qb * C::PBLK + i * C::KPL) = pf[qb][i];
+                }
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < C::NQ2; ++qb) {
+                    dp[qb] = f32x16{};
                     frag da[C::NSD];
                     load_row_frags<T, D>(da, tdO, qb * 32 + rsigma(l32), h);
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], vf[st], dp);
-                }
-                float lv[16], dl[16];
-#pragma unroll
-                for (int hr = 0; hr < 2; ++hr) {
-                    const int base = qb * 32 + 16 * hr + 8 * h;
-                    const f32x4 l0 = *reinterpret_cast<const f32x4 *>(wL + base);
-                    const f32x4 l1 = *reinterpret_cast<const f32x4 *>(wL + base + 4);
-                    const f32x4 d0 = *reinterpret_cast<const f32x4 *>(wD + base);
-                    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(wD + base + 4);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        lv[8 * hr + t] = l0[t] * kLog2e;
-                        lv[8 * hr + 4 + t] = l1[t] * kLog2e;
-                        dl[8 * hr + t] = d0[t];
-                        dl[8 * hr + 4 + t] = d1[t];
-                    }
-                }
-                // query q0 + 32*qb + ridx(r, h) is kept iff it is at least `lo` and below `hi`
-                const int lo = (causal ? key : 0) - q0 - 32 * qb - 2 * h;
-                const int hi = S - q0 - 32 * qb - 2 * h;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
-                    if (need_mask) {
-                        const int e = ridx(r, 0);
-                        p = (e >= lo && e < hi) ? p : 0.f;
-                    }
-                    s[r] = p;
-                    dp[r] = p * (dp[r] - dl[r]);  // Eq. 17
-                }
-                frag pf[C::NI], sf[C::NI];
-                to_bfrag<T>(pf, s);
-                to_bfrag<T>(sf, dp);
-#pragma unroll
-                for (int db = 0; db < C::ND; ++db) {
-                    frag a[C::NI];
-                    tr.load(a, tdO, qb, db);
-#pragma unroll
-                    for (int i = 0; i < C::NI; ++i) dV[db] = M::run(a[i], pf[i], dV[db]);  // Eq. 15
-                    tr.load(a, tQ, qb, db);
-#pragma unroll
-                    for (int i = 0; i < C::NI; ++i) dK[db] = M::run(a[i], sf[i], dK[db]);  // Eq. 19
+                    for (int st = 0; st < C::NSD; ++st) dp[qb] = M::run(da[st], bf[st], dp[qb]);  // Eq. 16
                 }
             }
         }
         wait_lgkm0();
-        lds_barrier();
+        lds_barrier();  // P of every pair is in LDS
+        if (active) {
+            if (role == 0) {
+#pragma unroll
+                for (int qb = 0; qb < C::NQ2; ++qb)
+#pragma unroll
+                    for (int db = 0; db < C::ND; ++db) {
+                        frag a[C::NI];
+                        tr.load(a, tdO, qb, db);
+#pragma unroll
+                        for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], pf[qb][i], acc[db]);  // Eq. 15
+                    }
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < C::NQ2; ++qb) {
+                    frag pr[C::NI];
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i)
+                        pr[i] = *reinterpret_cast<const typename M::frag *>(pbuf + qb * C::PBLK + i * C::KPL);
+                    float dl[16];
+                    stat(dl, qb, 1.f);
+                    f32x16 ds;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p;
+                        if constexpr (C::KPL == 8)
+                            p = (float)pr[r / 8][r % 8];
+                        else
+                            p = pr[r];
+                        ds[r] = p * (dp[qb][r] - dl[r]);  // Eq. 17
+                    }
+                    frag sf[C::NI];
+                    to_bfrag<T>(sf, ds);
+#pragma unroll
+                    for (int db = 0; db < C::ND; ++db) {
+                        frag a[C::NI];
+                        tr.load(a, tQ, qb, db);
+#pragma unroll
+                        for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], sf[i], acc[db]);  // Eq. 19
+                    }
+                }
+            }
+        }
+        wait_lgkm0();
+        lds_barrier();  // every wave is done with this stage and with P
     };
     for (int it = i0; it < nq2; it += 2) {
-        step(sQ0, sdO0, sL0, sD0, sQ1, sdO1, sL1, sD1, it);
-        if (it + 1 < nq2) step(sQ1, sdO1, sL1, sD1, sQ0, sdO0, sL0, sD0, it + 1);
+        step(sQ0, sdO0, sX0, sQ1, sdO1, sX1, it);
+        if (it + 1 < nq2) step(sQ1, sdO1, sX1, sQ0, sdO0, sX0, it + 1);
     }
     wait_vmcnt<0>();
 
     if (key < S) {
+        T *out = role ? dk : dv;
+        const float mul = role ? scale : 1.f;
 #pragma unroll
         for (int db = 0; db < C::ND; ++db)
 #pragma unroll
             for (int hr = 0; hr < 2; ++hr) {
                 const int d0 = db * 32 + 16 * hr + 8 * h;
-                if (d0 < D) {
-                    store8<T>(dk + (size_t)key * D + d0, dK[db], 8 * hr, scale);
-                    store8<T>(dv + (size_t)key * D + d0, dV[db], 8 * hr, 1.f);
-                }
+                if (d0 < D) store8<T>(out + (size_t)key * D + d0, acc[db], 8 * hr, mul);
             }
     }
 }
@@ -430,7 +480,7 @@ template <typename T, int D>
 static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                    const float *delta, void *dq, void *dk, void *dv, int BH, int S, float scale,
                    int causal, hipStream_t stream) {
-    using KC = KvTile<T, D, (sizeof(T) == 4 && D > 64) ? 32 : 64, 4>;
+    using KC = KvTile<T, D, (sizeof(T) == 4 && D > 64) ? 32 : 64>;
     using QC = QTile<T, D, 1, 64, 4>;
     const float c = scale * kLog2e;
     const long long g1 = (long long)((S + KC::BKV - 1) / KC::BKV) * BH;
