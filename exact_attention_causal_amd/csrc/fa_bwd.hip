@@ -90,7 +90,9 @@ struct KvTile {
     static constexpr int NI = 16 / KPL;
     using DMA = TileDma<T, D, BQ2, NW / 2>;           // the P waves load Q, the dS waves dO
     using PD = typename DMA::PD;
-    static constexpr int TILE = DMA::ELEMS;           // elements per Q or dO tile
+    // a Q (dO) tile array also carries the tile's L (D) values, 64 per P (dS) wave
+    static constexpr int XOFF = DMA::ELEMS;           // element offset of those values
+    static constexpr int TILE = DMA::ELEMS + NPAIR * kWave * 4 / (int)sizeof(T);
     static constexpr int PBLK = 64 * 16;              // P values of one 32x32 block (elements)
     static_assert(D % 16 == 0 && BQ2 % 32 == 0 && BQ2 <= kWave, "tile shape");
 };
@@ -105,12 +107,12 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, BQ2 = C::BQ2;
-    // Two stages of Q and dO tiles (each its own array, see the forward
-    // kernel) and of the tile's L (P waves) or D (dS waves) values, one
-    // 64-entry copy per wave; plus the P hand-over buffer.
-    __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE];
-    __shared__ __attribute__((aligned(16))) float sX0[C::NW * kWave], sX1[C::NW * kWave];
+    // Three stages of Q and dO tiles (each its own array, see the forward
+    // kernel; a Q array also holds the tile's L values, a dO array its D
+    // values -- keeping the number of DMA targets within what the compiler
+    // tracks), plus the P hand-over buffer.
+    __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE], sQ2[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE], sdO2[C::TILE];
     __shared__ __attribute__((aligned(16))) T sP[C::NPAIR * C::NQ2 * C::PBLK];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -156,8 +158,9 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     typedef __attribute__((address_space(3))) void lds_void;
     // Q (P waves) or dO (dS waves) rows, and L (P waves) or D (dS waves) of
     // query tile `it` (rows past the end load the last row; they are masked)
-    auto issue = [&](T *nQ, T *ndO, float *nX, int it) {
-        dma.issue(role ? ndO : nQ, role ? dout : q, it * BQ2, S, pair);
+    auto issue = [&](T *nQ, T *ndO, int it) {
+        T *dst = role ? ndO : nQ;
+        dma.issue(dst, role ? dout : q, it * BQ2, S, pair);
         // slot j holds the query a lane half reads as registers 8u..8u+7 of its
         // 32-query block: slot 16u + 8h + 4rr + e <-> query ridx(8u + 4rr + e, h),
         // so each half reads two runs of 8 slots
@@ -165,17 +168,17 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                        2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
         const int qi = min(it * BQ2 + jq, S - 1);
         __builtin_amdgcn_global_load_lds((const void *)((role ? delta : lse) + qi),
-                                         (lds_void *)(nX + wave * kWave), 4, 0, 0);
+                                         (lds_void *)(dst + C::XOFF + pair * kWave * 4 / (int)sizeof(T)), 4, 0, 0);
     };
-    issue(sQ0, sdO0, sX0, i0);
+    issue(sQ0, sdO0, i0);
+    issue(sQ1, sdO1, i0 + 1);
 
-    auto step = [&](const T *tQ, const T *tdO, const float *tX, T *nQ, T *ndO, float *nX, int it) {
+    auto step = [&](const T *tQ, const T *tdO, T *nQ, T *ndO, int it) {
         const int q0 = it * BQ2;
-        // prefetch query tile it+1 unconditionally (see the forward kernel)
-        issue(nQ, ndO, nX, it + 1);
-        wait_vmcnt<C::DMA::IPW + 1>();
-        lds_barrier();
-        const float *wX = tX + wave * kWave;
+        wait_vmcnt<C::DMA::IPW + 1>();  // query tile it has landed (it+1 may be in flight)
+        lds_barrier();                  // ... for every wave; tile it-1's stage and P are released
+        issue(nQ, ndO, it + 2);         // unconditionally (see the forward kernel)
+        const float *wX = reinterpret_cast<const float *>((role ? tdO : tQ) + C::XOFF) + pair * kWave;
         const bool active = kw0 < S && !(causal && q0 + BQ2 - 1 < kw0);
         const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
         // this wave's per-query statistic for registers r of block qb
@@ -282,12 +285,12 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                 }
             }
         }
-        wait_lgkm0();
-        lds_barrier();  // every wave is done with this stage and with P
+        wait_lgkm0();  // this wave's reads of the stage and of P are complete
     };
-    for (int it = i0; it < nq2; it += 2) {
-        step(sQ0, sdO0, sX0, sQ1, sdO1, sX1, it);
-        if (it + 1 < nq2) step(sQ1, sdO1, sX1, sQ0, sdO0, sX0, it + 1);
+    for (int it = i0; it < nq2; it += 3) {
+        step(sQ0, sdO0, sQ2, sdO2, it);
+        if (it + 1 < nq2) step(sQ1, sdO1, sQ0, sdO0, it + 1);
+        if (it + 2 < nq2) step(sQ2, sdO2, sQ1, sdO1, it + 2);
     }
     wait_vmcnt<0>();
 
@@ -316,9 +319,9 @@ struct QTile {
     static constexpr int NKB = BK / 32;
     static constexpr int ND = (D + 31) / 32;
     static constexpr int NI = 16 / KPL;
-    using DMA = TileDma<T, D, BK, NW>;
+    using DMA = TileDma<T, D, BK, NW / 2>;           // half the waves load K, half V
     static constexpr int TILE = DMA::ELEMS;           // elements per K or V tile
-    static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
+    static_assert(D % 16 == 0 && BK % 32 == 0 && NW % 2 == 0, "tile shape");
 };
 
 template <typename T, typename C>
@@ -331,9 +334,9 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
-    // two stages of K and V tiles, each its own array (see the forward kernel)
-    __shared__ __attribute__((aligned(1024))) T sK0[C::TILE], sK1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) T sV0[C::TILE], sV1[C::TILE];
+    // three stages of K and V tiles, each its own array (see the forward kernel)
+    __shared__ __attribute__((aligned(1024))) T sK0[C::TILE], sK1[C::TILE], sK2[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sV0[C::TILE], sV1[C::TILE], sV2[C::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -384,17 +387,17 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
 
     typename C::DMA dma;
-    dma.init(lane, wave);
-    dma.issue(sK0, k, 0, S, wave);
-    dma.issue(sV0, v, 0, S, wave);
+    const int half = wave / (C::NW / 2), hw = wave % (C::NW / 2);
+    dma.init(lane, hw);
+    auto issue = [&](T *nK, T *nV, int j) { dma.issue(half ? nV : nK, half ? v : k, j * BK, S, hw); };
+    issue(sK0, sV0, 0);
+    issue(sK1, sV1, 1);
 
     auto step = [&](const T *tK, const T *tV, T *nK, T *nV, int j) {
         const int j0 = j * BK;
-        // prefetch tile j+1 unconditionally (see the forward kernel)
-        dma.issue(nK, k, j0 + BK, S, wave);
-        dma.issue(nV, v, j0 + BK, S, wave);
-        wait_vmcnt<2 * C::DMA::IPW>();
+        wait_vmcnt<C::DMA::IPW>();
         lds_barrier();
+        issue(nK, nV, j + 2);  // unconditionally (see the forward kernel)
         const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
         if (active) {
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
@@ -441,11 +444,11 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
             }
         }
         wait_lgkm0();
-        lds_barrier();
     };
-    for (int j = 0; j < nkt; j += 2) {
-        step(sK0, sV0, sK1, sV1, j);
+    for (int j = 0; j < nkt; j += 3) {
+        step(sK0, sV0, sK2, sV2, j);
         if (j + 1 < nkt) step(sK1, sV1, sK0, sV0, j + 1);
+        if (j + 2 < nkt) step(sK2, sV2, sK1, sV1, j + 2);
     }
     wait_vmcnt<0>();
 
@@ -481,7 +484,7 @@ static int bwd_for(const void *q, const void *k, const void *v, const void *dout
                    const float *delta, void *dq, void *dk, void *dv, int BH, int S, float scale,
                    int causal, hipStream_t stream) {
     using KC = KvTile<T, D, (sizeof(T) == 4 && D > 64) ? 32 : 64>;
-    using QC = QTile<T, D, 1, 64, 4>;
+    using QC = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
     const float c = scale * kLog2e;
     const long long g1 = (long long)((S + KC::BKV - 1) / KC::BKV) * BH;
     const int nqt = (S + QC::BQ - 1) / QC::BQ;

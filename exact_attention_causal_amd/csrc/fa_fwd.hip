@@ -25,8 +25,8 @@
 //   * the accumulator is rescaled only when a new score exceeds the running
 //     maximum by 2^8 (exactness is kept because O and l share the stale max);
 //   * K/V tiles are loaded straight into LDS (global_load_lds_dwordx4) into
-//     two stages, so the next tile streams in while the current one is used
-//     and no registers or VALU work are spent staging it;
+//     three stages, so the next two tiles stream in while the current one is
+//     used and no registers or VALU work are spent staging them;
 //   * workgroups are dispatched longest-first (highest query tile first) so
 //     the short causal tiles fill in the tail.
 #include "fa_common.hpp"
@@ -44,9 +44,9 @@ struct FwdTile {
     static constexpr int NKB = BK / 32;               // 32-key blocks per tile
     static constexpr int ND = (D + 31) / 32;          // 32-row output blocks over d
     static constexpr int NI = 16 / KPL;               // MFMAs per 32-key reduction block
-    using DMA = TileDma<T, D, BK, NW>;
+    using DMA = TileDma<T, D, BK, NW / 2>;           // half the waves load K, half V
     static constexpr int TILE = DMA::ELEMS;           // elements per K or V tile
-    static_assert(D % 16 == 0 && BK % 32 == 0, "tile shape");
+    static_assert(D % 16 == 0 && BK % 32 == 0 && NW % 2 == 0, "tile shape");
 };
 
 // Scores more than 2^kRescaleSlack above the running maximum force a rescale;
@@ -62,12 +62,12 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
-    // Two stages of K and V tiles: the next tile streams in while this one is
-    // used.  Each stage is its own array and the loop is unrolled by two, so
-    // the compiler can see that reads of one stage never alias the DMA into
-    // the other and does not wait for the in-flight tile.
-    __shared__ __attribute__((aligned(1024))) T sK0[C::TILE], sK1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) T sV0[C::TILE], sV1[C::TILE];
+    // Three stages of K and V tiles: two tiles stream in while one is used.
+    // Each stage is its own array and the loop is unrolled by three, so the
+    // compiler can see that reads of one stage never alias the DMA into the
+    // others and does not wait for the tiles in flight.
+    __shared__ __attribute__((aligned(1024))) T sK0[C::TILE], sK1[C::TILE], sK2[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sV0[C::TILE], sV1[C::TILE], sV2[C::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,20 +112,22 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
 
     typename C::DMA dma;
-    dma.init(lane, wave);
-    dma.issue(sK0, k, 0, S, wave);
-    dma.issue(sV0, v, 0, S, wave);
+    const int half = wave / (C::NW / 2), hw = wave % (C::NW / 2);
+    dma.init(lane, hw);
+    // this wave's share of key/value tile j: K (first half of the waves) or V
+    auto issue = [&](T *nK, T *nV, int j) { dma.issue(half ? nV : nK, half ? v : k, j * BK, S, hw); };
+    issue(sK0, sV0, 0);
+    issue(sK1, sV1, 1);
 
     auto step = [&](const T *tK, const T *tV, T *nK, T *nV, int j) {
         const int j0 = j * BK;
-        // Prefetch tile j+1 into the other stage (released by the barrier that
-        // ended the previous step).  It is issued unconditionally -- past the
-        // last tile it re-reads valid rows nobody uses -- because a conditional
-        // issue makes the compiler wait for every DMA before the next LDS read.
-        dma.issue(nK, k, j0 + BK, S, wave);
-        dma.issue(nV, v, j0 + BK, S, wave);
-        wait_vmcnt<2 * C::DMA::IPW>();  // this wave's part of tile j has landed
-        lds_barrier();                  // every wave's part of tile j has landed
+        wait_vmcnt<C::DMA::IPW>();  // this wave's part of tile j has landed (j+1 may be in flight)
+        lds_barrier();              // every part of tile j landed; stage of tile j-1 released
+        // Prefetch tile j+2 into the stage tile j-1 used.  It is issued
+        // unconditionally -- past the last tile it re-reads valid rows nobody
+        // uses -- because a conditional issue makes the compiler wait for every
+        // DMA before the next LDS read.
+        issue(nK, nV, j + 2);
         const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
         if (active) {
             // S^T block (kb, qb): rows = keys j0 + 32*kb + ridx(r, h), col = query.
@@ -206,12 +208,12 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
                 }
             }
         }
-        wait_lgkm0();
-        lds_barrier();  // every wave is done reading this stage
+        wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
     };
-    for (int j = 0; j < nkt; j += 2) {
-        step(sK0, sV0, sK1, sV1, j);
+    for (int j = 0; j < nkt; j += 3) {
+        step(sK0, sV0, sK2, sV2, j);
         if (j + 1 < nkt) step(sK1, sV1, sK0, sV0, j + 1);
+        if (j + 2 < nkt) step(sK2, sV2, sK1, sV1, j + 2);
     }
     wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it exits
 
@@ -249,7 +251,9 @@ static int run_fwd(const void *q, const void *k, const void *v, void *o, float *
 template <typename T, int D>
 static int fwd_for(const void *q, const void *k, const void *v, void *o, float *lse, int BH, int S,
                    float scale, int causal, hipStream_t stream) {
-    return run_fwd<T, FwdTile<T, D, 1, 64, 4>>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    // fp32 rows are twice the bytes: wide fp32 heads take 32-key tiles to fit three stages
+    constexpr int BK = (sizeof(T) == 4 && D > 80) ? 32 : 64;
+    return run_fwd<T, FwdTile<T, D, 1, BK, 8>>(q, k, v, o, lse, BH, S, scale, causal, stream);
 }
 
 template <typename T>
