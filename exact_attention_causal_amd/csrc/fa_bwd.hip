@@ -216,13 +216,14 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                     const int lo = (causal ? key : 0) - q0 - 32 * qb - 2 * h;
                     const int hi = S - q0 - 32 * qb - 2 * h;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float p = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
-                        if (need_mask) {
+                    for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
+                    if (need_mask) {
+                        asm volatile("");  // a real branch: only diagonal / tail tiles pay for masking
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
                             const int e = ridx(r, 0);
-                            p = (e >= lo && e < hi) ? p : 0.f;
+                            s[r] = (e >= lo && e < hi) ? s[r] : 0.f;
                         }
-                        s[r] = p;
                     }
                     to_bfrag<T>(pf[qb], s);
                     // hand P to the partner (same lane layout on both sides)
@@ -426,11 +427,14 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
                     const int qi = qw0 + qb * 32 + l32;
                     const int t = (causal ? min(qi + 1, S) : S) - j0 - 32 * kb - 2 * h;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float p = fast_exp2(fmaf(s[r], c, -lq[qb]));  // Eq. 14
-                        if (need_mask) p = (ridx(r, 0) < t) ? p : 0.f;
-                        dp[r] = p * (dp[r] - dl[qb]);  // Eq. 17
+                    for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lq[qb]));  // Eq. 14
+                    if (need_mask) {
+                        asm volatile("");  // a real branch: only diagonal / tail tiles pay for masking
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[r] = (ridx(r, 0) < t) ? s[r] : 0.f;
                     }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dl[qb]);  // Eq. 17
                     frag sf[C::NI];
                     to_bfrag<T>(sf, dp);
 #pragma unroll

@@ -146,6 +146,9 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
             }
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
             if (need_mask) {
+                // (the empty volatile asm keeps this block a real branch: only
+                // tiles crossing the diagonal or the sequence end pay for masking)
+                asm volatile("");
                 // key j0 + 32*kb + ridx(r, h) is kept iff it is below `lim`
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
