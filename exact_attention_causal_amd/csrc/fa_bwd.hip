@@ -158,9 +158,8 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     typedef __attribute__((address_space(3))) void lds_void;
     // Q (P waves) or dO (dS waves) rows, and L (P waves) or D (dS waves) of
     // query tile `it` (rows past the end load the last row; they are masked)
-    auto issue = [&](T *nQ, T *ndO, int it) {
+    auto issue_x = [&](T *nQ, T *ndO, int it) {
         T *dst = role ? ndO : nQ;
-        dma.issue(dst, role ? dout : q, it * BQ2, S, pair);
         // slot j holds the query a lane half reads as registers 8u..8u+7 of its
         // 32-query block: slot 16u + 8h + 4rr + e <-> query ridx(8u + 4rr + e, h),
         // so each half reads two runs of 8 slots
@@ -170,6 +169,10 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         __builtin_amdgcn_global_load_lds((const void *)((role ? delta : lse) + qi),
                                          (lds_void *)(dst + C::XOFF + pair * kWave * 4 / (int)sizeof(T)), 4, 0, 0);
     };
+    auto issue = [&](T *nQ, T *ndO, int it) {
+        dma.issue(role ? ndO : nQ, role ? dout : q, it * BQ2, S, pair);
+        issue_x(nQ, ndO, it);
+    };
     issue(sQ0, sdO0, i0);
     issue(sQ1, sdO1, i0 + 1);
 
@@ -177,12 +180,19 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         const int q0 = it * BQ2;
         wait_vmcnt<C::DMA::IPW + 1>();  // query tile it has landed (it+1 may be in flight)
         lds_barrier();                  // ... for every wave; tile it-1's stage and P are released
-        issue(nQ, ndO, it + 2);         // unconditionally (see the forward kernel)
-        const float *wX = reinterpret_cast<const float *>((role ? tdO : tQ) + C::XOFF) + pair * kWave;
+        // prefetch of tile it+2, unconditional and spread over the query
+        // blocks of both halves of the step (see the forward kernel)
+        constexpr int NP = 2 * C::NQ2;
+        const auto rs = C::DMA::range(role ? dout : q, (it + 2) * BQ2, S);
+        T *const nT = role ? ndO : nQ;
+        issue_x(nQ, ndO, it + 2);
         const bool active = kw0 < S && !(causal && q0 + BQ2 - 1 < kw0);
         const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
-        // this wave's per-query statistic for registers r of block qb
-        auto stat = [&](float (&x)[16], int qb, float mul) {
+        // this wave's per-query statistic (L from a Q tile, D from a dO tile)
+        // for registers r of block qb (the tile is named directly in each role
+        // so the compiler knows which DMA target the read depends on)
+        auto stat = [&](float (&x)[16], const T *tile, int qb, float mul) {
+            const float *wX = reinterpret_cast<const float *>(tile + C::XOFF) + pair * kWave;
 #pragma unroll
             for (int hr = 0; hr < 2; ++hr) {
                 const int base = qb * 32 + 16 * hr + 8 * h;
@@ -198,10 +208,12 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         T *pbuf = sP + pair * C::NQ2 * C::PBLK + lane * 16;
         f32x16 dp[C::NQ2];
         frag pf[C::NQ2][C::NI];
+        if (!active) dma.issue(nT, role ? dout : q, (it + 2) * BQ2, S, pair);
         if (active) {
             if (role == 0) {
 #pragma unroll
                 for (int qb = 0; qb < C::NQ2; ++qb) {
+                    dma.template issue_part<NP>(qb, nT, rs, pair);
                     // S block: rows = queries q0 + 32*qb + ridx(r, h), col = key.
                     f32x16 s = f32x16{};
                     {
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                         for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], bf[st], s);
                     }
                     float lv[16];
-                    stat(lv, qb, kLog2e);
+                    stat(lv, tQ, qb, kLog2e);
                     // query q0 + 32*qb + ridx(r, h) is kept iff it is at least `lo` and below `hi`
                     const int lo = (causal ? key : 0) - q0 - 32 * qb - 2 * h;
                     const int hi = S - q0 - 32 * qb - 2 * h;
@@ -234,6 +246,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
             } else {
 #pragma unroll
                 for (int qb = 0; qb < C::NQ2; ++qb) {
+                    dma.template issue_part<NP>(qb, nT, rs, pair);
                     dp[qb] = f32x16{};
                     frag da[C::NSD];
                     load_row_frags<T, D>(da, tdO, qb * 32 + rsigma(l32), h);
@@ -247,7 +260,8 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         if (active) {
             if (role == 0) {
 #pragma unroll
-                for (int qb = 0; qb < C::NQ2; ++qb)
+                for (int qb = 0; qb < C::NQ2; ++qb) {
+                    dma.template issue_part<NP>(C::NQ2 + qb, nT, rs, pair);
 #pragma unroll
                     for (int db = 0; db < C::ND; ++db) {
                         frag a[C::NI];
@@ -255,15 +269,17 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 #pragma unroll
                         for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], pf[qb][i], acc[db]);  // Eq. 15
                     }
+                }
             } else {
 #pragma unroll
                 for (int qb = 0; qb < C::NQ2; ++qb) {
+                    dma.template issue_part<NP>(C::NQ2 + qb, nT, rs, pair);
                     frag pr[C::NI];
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i)
                         pr[i] = *reinterpret_cast<const typename M::frag *>(pbuf + qb * C::PBLK + i * C::KPL);
                     float dl[16];
-                    stat(dl, qb, 1.f);
+                    stat(dl, tdO, qb, 1.f);
                     f32x16 ds;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -398,13 +414,19 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
         const int j0 = j * BK;
         wait_vmcnt<C::DMA::IPW>();
         lds_barrier();
-        issue(nK, nV, j + 2);  // unconditionally (see the forward kernel)
+        // prefetch of tile j+2, unconditional and spread over the key blocks
+        // (see the forward kernel)
+        const auto rs = C::DMA::range(half ? v : k, (j + 2) * BK, S);
+        T *const nT = half ? nV : nK;
         const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
-        if (active) {
+        if (!active) {
+            dma.issue(nT, half ? v : k, (j + 2) * BK, S, hw);
+        } else {
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 __builtin_amdgcn_sched_barrier(0);
+                dma.template issue_part<C::NKB>(kb, nT, rs, hw);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     // S^T block: rows = keys j0 + 32*kb + ridx(r, h), col = query.

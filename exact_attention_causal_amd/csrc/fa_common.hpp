@@ -145,42 +145,65 @@ struct Pad {
     static_assert(((PITCH * sizeof(T) / 4) % 8) == 4, "pitch must be 4 (mod 8) words");
 };
 
-// Direct global -> LDS tile loads (global_load_lds_dwordx4): each instruction
-// of a wave writes 1 KiB of consecutive LDS (16 bytes per lane, in lane
-// order), so each lane fetches the global chunk that belongs at its LDS slot.
-// The tile's slots are rounded up to whole instructions for every wave; slots
-// past the last row, pad slots and rows past the end of the sequence all fetch
-// a valid (clamped) chunk: the values are finite, and the kernels mask those
-// rows or never use what lands in the pad.
+// Direct global -> LDS tile loads (buffer_load_dwordx4 ... lds): each
+// instruction of a wave writes 1 KiB of consecutive LDS (16 bytes per lane, in
+// lane order), so each lane fetches the global chunk that belongs at its LDS
+// slot.  The tile's slots are rounded up to whole instructions for every wave.
+// The loads go through a buffer descriptor whose range ends at the last row of
+// the tile that exists: slots past the tile's last row, pad slots and rows past
+// the end of the sequence are out of range, so they fetch nothing from memory
+// and land as zeros (the kernels mask those rows or never read the pad).
 template <typename T, int D, int R, int NW>
 struct TileDma {
     using PD = Pad<T, D>;
     static constexpr int NSLOT = R * PD::SLOTS;
     static constexpr int IPW = (NSLOT + 64 * NW - 1) / (64 * NW);  // instructions per wave
     static constexpr int ELEMS = IPW * NW * 64 * PD::CW;          // tile allocation (elements)
+    static constexpr int kNone = 0x40000000;                      // beyond any tile's range
     // transposed reads of the last 32-column block may run up to 32 elements past a row
     static_assert(R * PD::PITCH + 32 <= ELEMS || PD::CPR * PD::CW % 32 == 0, "tile slack");
-    int row[IPW];  // row within the tile
-    int col[IPW];  // element column of the chunk
+    static_assert((long long)R * D * sizeof(T) < kNone, "tile range");
+    int voff[IPW];  // byte offset of this lane's chunk from the tile's first row, or kNone
 
     __device__ inline void init(int lane, int wave) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int p = (wave * IPW + i) * 64 + lane;  // 16-byte slot within the tile
-            row[i] = min(p / PD::SLOTS, R - 1);
-            col[i] = min(p % PD::SLOTS, PD::CPR - 1) * PD::CW;
+            const int r = p / PD::SLOTS, cc = p % PD::SLOTS;
+            voff[i] = (r < R && cc < PD::CPR) ? (r * D + cc * PD::CW) * (int)sizeof(T) : kNone;
         }
     }
-    // Issue this wave's share of the tile holding rows row0 .. row0 + R - 1.
-    __device__ inline void issue(T *lds, const T *base, int row0, int S, int wave) const {
+    // Descriptor of rows row0 .. min(row0 + R, S) - 1 of a [S, D] matrix
+    // (empty when row0 >= S).  All arguments are wave-uniform.
+    static __device__ inline __amdgpu_buffer_rsrc_t range(const T *base, int row0, int S) {
+        // (the clamp is selected as a vector min/max; readfirstlane hands the
+        // uniform result back to the scalar unit, where the descriptor lives)
+        const int rows = __builtin_amdgcn_readfirstlane(max(0, min(R, S - row0)));
+        // dword 3: 32-bit data format (the raw-buffer setting for gfx9 parts)
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(base + (size_t)row0 * D), 0,
+                                                 rows * D * (int)sizeof(T), 0x00020000);
+    }
+    // Issue instruction i of this wave's share of the tile described by `rs`
+    // (kernels spread the instructions over their work so the waves of a
+    // workgroup do not all queue at the memory pipeline at once).
+    __device__ inline void issue_one(int i, T *lds, __amdgpu_buffer_rsrc_t rs, int wave) const {
         typedef __attribute__((address_space(3))) void lds_void;
+        T *dst = lds + (wave * IPW + i) * (1024 / (int)sizeof(T));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff[i], 0, 0, 0);
+    }
+    // Issue part p of NP near-equal parts of this wave's share.
+    template <int NP>
+    __device__ inline void issue_part(int p, T *lds, __amdgpu_buffer_rsrc_t rs, int wave) const {
+        const int a = (IPW * p + NP - 1) / NP, b = (IPW * (p + 1) + NP - 1) / NP;
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int r = min(row0 + row[i], S - 1);
-            T *dst = lds + (wave * IPW + i) * (1024 / (int)sizeof(T));
-            __builtin_amdgcn_global_load_lds((const void *)(base + (size_t)r * D + col[i]),
-                                             (lds_void *)dst, 16, 0, 0);
-        }
+        for (int i = 0; i < IPW; ++i)
+            if (i >= a && i < b) issue_one(i, lds, rs, wave);
+    }
+    // Issue this wave's whole share of the tile holding rows row0 .. row0 + R - 1.
+    __device__ inline void issue(T *lds, const T *base, int row0, int S, int wave) const {
+        const __amdgpu_buffer_rsrc_t rs = range(base, row0, S);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) issue_one(i, lds, rs, wave);
     }
 };
 

@@ -123,17 +123,24 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
         const int j0 = j * BK;
         wait_vmcnt<C::DMA::IPW>();  // this wave's part of tile j has landed (j+1 may be in flight)
         lds_barrier();              // every part of tile j landed; stage of tile j-1 released
-        // Prefetch tile j+2 into the stage tile j-1 used.  It is issued
-        // unconditionally -- past the last tile it re-reads valid rows nobody
-        // uses -- because a conditional issue makes the compiler wait for every
-        // DMA before the next LDS read.
-        issue(nK, nV, j + 2);
+        // Prefetch tile j+2 into the stage tile j-1 used, one instruction at
+        // a time spread over this step's work.  It is issued unconditionally
+        // -- past the last tile its range is empty and it fetches nothing --
+        // because a conditional issue makes the compiler wait for every DMA
+        // before the next LDS read.
+        // (parts: one before each S^T block and each O^T block)
+        constexpr int NP = 2 * C::NKB;
+        const auto rs = C::DMA::range(half ? v : k, (j + 2) * BK, S);
+        T *const nT = half ? nV : nK;
         const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
-        if (active) {
+        if (!active) {
+            dma.issue(nT, half ? v : k, (j + 2) * BK, S, hw);
+        } else {
             // S^T block (kb, qb): rows = keys j0 + 32*kb + ridx(r, h), col = query.
             f32x16 s[NQB][C::NKB];
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
+                dma.template issue_part<NP>(kb, nT, rs, hw);
                 frag kf[C::NSD];
                 load_row_frags<T, D>(kf, tK, kb * 32 + rsigma(l32), h);
 #pragma unroll
@@ -197,6 +204,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
             // O^T += V^T P^T
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
+                dma.template issue_part<NP>(C::NKB + kb, nT, rs, hw);
                 frag pf[NQB][C::NI];
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) to_bfrag<T>(pf[qb], s[qb][kb]);
