@@ -72,10 +72,15 @@ __global__ __launch_bounds__(256) void delta_kernel(const T *__restrict__ o, con
 // products between them (no product is computed twice):
 //   * the P wave forms S = Q K^T, P = exp(S - L) (Eq. 13-14), hands P to its
 //     partner through LDS and accumulates dV^T += dO^T P (Eq. 15);
-//   * the dS wave forms dP = dO V^T (Eq. 16) while its partner works on P,
-//     then dS = P o (dP - D) (Eq. 17) and accumulates dK^T += Q^T dS (Eq. 19).
+//   * the dS wave forms dP = dO V^T (Eq. 16), and dS = P o (dP - D) (Eq. 17)
+//     once its partner's P is there, and accumulates dK^T += Q^T dS (Eq. 19).
 // So each wave keeps one B operand (K^T or V^T) and one accumulator in
-// registers, which leaves room for two waves per SIMD.
+// registers, which leaves room for two waves per SIMD.  The pair runs one
+// query tile apart: in step i the P wave accumulates dV for tile i-1 and then
+// forms P of tile i, while the dS wave does all of its work for tile i-1
+// (whose P its partner wrote in step i-1).  One workgroup barrier per step
+// separates them, and each wave's vector work (exponentials, dS) overlaps its
+// partner's matrix products on the shared SIMD.
 
 template <typename T, int D_, int BQ2_>
 struct KvTile {
@@ -94,6 +99,7 @@ struct KvTile {
     static constexpr int XOFF = DMA::ELEMS;           // element offset of those values
     static constexpr int TILE = DMA::ELEMS + NPAIR * kWave * 4 / (int)sizeof(T);
     static constexpr int PBLK = 64 * 16;              // P values of one 32x32 block (elements)
+    static constexpr int PBUF = NPAIR * NQ2 * PBLK;   // P of one query tile (one of two buffers)
     static_assert(D % 16 == 0 && BQ2 % 32 == 0 && BQ2 <= kWave, "tile shape");
 };
 
@@ -107,13 +113,14 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, BQ2 = C::BQ2;
-    // Three stages of Q and dO tiles (each its own array, see the forward
-    // kernel; a Q array also holds the tile's L values, a dO array its D
-    // values -- keeping the number of DMA targets within what the compiler
-    // tracks), plus the P hand-over buffer.
+    // Three stages of Q and dO tiles, each its own array (see the forward
+    // kernel): tile i-1 (read transposed), tile i (read by rows) and tile i+1
+    // (in flight).  A Q array also holds the tile's L values, a dO array its
+    // D values -- keeping the number of DMA targets within what the compiler
+    // tracks.  Two P buffers: the one written in this step and the one read.
     __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE], sQ2[C::TILE];
     __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE], sdO2[C::TILE];
-    __shared__ __attribute__((aligned(16))) T sP[C::NPAIR * C::NQ2 * C::PBLK];
+    __shared__ __attribute__((aligned(16))) T sP[2 * C::PBUF];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -152,14 +159,17 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 
     const int nq2 = (S + BQ2 - 1) / BQ2;
     const int i0 = causal ? k0 / BQ2 : 0;
+    const int ntile = nq2 - i0;
 
     typename C::DMA dma;
     dma.init(lane, pair);
     typedef __attribute__((address_space(3))) void lds_void;
     // Q (P waves) or dO (dS waves) rows, and L (P waves) or D (dS waves) of
-    // query tile `it` (rows past the end load the last row; they are masked)
-    auto issue_x = [&](T *nQ, T *ndO, int it) {
+    // query tile `it` (rows past the end are out of range and land as zeros;
+    // the statistics of those rows repeat the last row's; all are masked)
+    auto issue = [&](T *nQ, T *ndO, int it) {
         T *dst = role ? ndO : nQ;
+        dma.issue(dst, role ? dout : q, it * BQ2, S, pair);
         // slot j holds the query a lane half reads as registers 8u..8u+7 of its
         // 32-query block: slot 16u + 8h + 4rr + e <-> query ridx(8u + 4rr + e, h),
         // so each half reads two runs of 8 slots
@@ -169,51 +179,66 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         __builtin_amdgcn_global_load_lds((const void *)((role ? delta : lse) + qi),
                                          (lds_void *)(dst + C::XOFF + pair * kWave * 4 / (int)sizeof(T)), 4, 0, 0);
     };
-    auto issue = [&](T *nQ, T *ndO, int it) {
-        dma.issue(role ? ndO : nQ, role ? dout : q, it * BQ2, S, pair);
-        issue_x(nQ, ndO, it);
+    // this wave's per-query statistic (L from a Q tile, D from a dO tile)
+    // for registers r of block qb (the tile is named directly in each role
+    // so the compiler knows which DMA target the read depends on)
+    auto stat = [&](float (&x)[16], const T *tile, int qb, float mul) {
+        const float *wX = reinterpret_cast<const float *>(tile + C::XOFF) + pair * kWave;
+#pragma unroll
+        for (int hr = 0; hr < 2; ++hr) {
+            const int base = qb * 32 + 16 * hr + 8 * h;
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(wX + base);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(wX + base + 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x[8 * hr + t] = a[t] * mul;
+                x[8 * hr + 4 + t] = b[t] * mul;
+            }
+        }
+    };
+    // tile it holds queries this pair's keys depend on
+    auto active = [&](int it) {
+        return it >= i0 && it < nq2 && kw0 < S && !(causal && it * BQ2 + BQ2 - 1 < kw0);
     };
     issue(sQ0, sdO0, i0);
-    issue(sQ1, sdO1, i0 + 1);
 
-    auto step = [&](const T *tQ, const T *tdO, T *nQ, T *ndO, int it) {
+
+    // Step u (query tile it = i0 + u): stage tQ holds Q of tile it, pQ/pdO
+    // hold tile it-1; nQ/ndO receive tile it+1 (the stages of tile it-2).
+    auto step = [&](const T *tQ, const T *pQ, const T *pdO, T *nQ, T *ndO, int u) {
+        const int it = i0 + u;
         const int q0 = it * BQ2;
-        wait_vmcnt<C::DMA::IPW + 1>();  // query tile it has landed (it+1 may be in flight)
-        lds_barrier();                  // ... for every wave; tile it-1's stage and P are released
-        // prefetch of tile it+2, unconditional and spread over the query
-        // blocks of both halves of the step (see the forward kernel)
-        constexpr int NP = 2 * C::NQ2;
-        const auto rs = C::DMA::range(role ? dout : q, (it + 2) * BQ2, S);
-        T *const nT = role ? ndO : nQ;
-        issue_x(nQ, ndO, it + 2);
-        const bool active = kw0 < S && !(causal && q0 + BQ2 - 1 < kw0);
-        const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
-        // this wave's per-query statistic (L from a Q tile, D from a dO tile)
-        // for registers r of block qb (the tile is named directly in each role
-        // so the compiler knows which DMA target the read depends on)
-        auto stat = [&](float (&x)[16], const T *tile, int qb, float mul) {
-            const float *wX = reinterpret_cast<const float *>(tile + C::XOFF) + pair * kWave;
-#pragma unroll
-            for (int hr = 0; hr < 2; ++hr) {
-                const int base = qb * 32 + 16 * hr + 8 * h;
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(wX + base);
-                const f32x4 b = *reinterpret_cast<const f32x4 *>(wX + base + 4);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    x[8 * hr + t] = a[t] * mul;
-                    x[8 * hr + 4 + t] = b[t] * mul;
-                }
-            }
-        };
-        T *pbuf = sP + pair * C::NQ2 * C::PBLK + lane * 16;
-        f32x16 dp[C::NQ2];
-        frag pf[C::NQ2][C::NI];
-        if (!active) dma.issue(nT, role ? dout : q, (it + 2) * BQ2, S, pair);
-        if (active) {
-            if (role == 0) {
+        wait_vmcnt<0>();  // this wave's part of tile it has landed
+        lds_barrier();    // every part of it; P of tile it-1 is written; the stages of tile it-2 are free
+        // Tile it+1 is issued whole and unconditionally (see the forward
+        // kernel); past the last tile its range is empty.
+        issue(nQ, ndO, it + 1);
+        const bool cur = active(it), prev = active(it - 1);
+        T *pw = sP + (u & 1) * C::PBUF + pair * C::NQ2 * C::PBLK + lane * 16;        // P of tile it
+        const T *pr = sP + ((u + 1) & 1) * C::PBUF + pair * C::NQ2 * C::PBLK + lane * 16;  // P of it-1
+        if (role == 0) {
+            if (prev) {
+                // dV^T += dO^T P for tile it-1, P read back from the buffer
+                // this wave wrote in the previous step
 #pragma unroll
                 for (int qb = 0; qb < C::NQ2; ++qb) {
-                    dma.template issue_part<NP>(qb, nT, rs, pair);
+                    frag pp[C::NI];
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i)
+                        pp[i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * C::KPL);
+#pragma unroll
+                    for (int db = 0; db < C::ND; ++db) {
+                        frag a[C::NI];
+                        tr.load(a, pdO, qb, db);
+#pragma unroll
+                        for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], pp[i], acc[db]);  // Eq. 15
+                    }
+                }
+            }
+            if (cur) {
+                const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
+#pragma unroll
+                for (int qb = 0; qb < C::NQ2; ++qb) {
                     // S block: rows = queries q0 + 32*qb + ridx(r, h), col = key.
                     f32x16 s = f32x16{};
                     {
@@ -237,77 +262,57 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                             s[r] = (e >= lo && e < hi) ? s[r] : 0.f;
                         }
                     }
-                    to_bfrag<T>(pf[qb], s);
+                    frag pf[C::NI];
+                    to_bfrag<T>(pf, s);
                     // hand P to the partner (same lane layout on both sides)
 #pragma unroll
-                    for (int i = 0; i < C::NI; ++i)
-                        *reinterpret_cast<typename M::frag *>(pbuf + qb * C::PBLK + i * C::KPL) = pf[qb][i];
+                    for (int i = 0; i < C::NI; ++i) *reinterpret_cast<frag *>(pw + qb * C::PBLK + i * C::KPL) = pf[i];
                 }
-            } else {
+            }
+        } else if (prev) {
+            // tile it-1: dP = dO V^T, dS = P o (dP - D), dK^T += Q^T dS
 #pragma unroll
-                for (int qb = 0; qb < C::NQ2; ++qb) {
-                    dma.template issue_part<NP>(qb, nT, rs, pair);
-                    dp[qb] = f32x16{};
+            for (int qb = 0; qb < C::NQ2; ++qb) {
+                f32x16 dp = f32x16{};
+                {
                     frag da[C::NSD];
-                    load_row_frags<T, D>(da, tdO, qb * 32 + rsigma(l32), h);
+                    load_row_frags<T, D>(da, pdO, qb * 32 + rsigma(l32), h);
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) dp[qb] = M::run(da[st], bf[st], dp[qb]);  // Eq. 16
+                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bf[st], dp);  // Eq. 16
+                }
+                frag pp[C::NI];
+#pragma unroll
+                for (int i = 0; i < C::NI; ++i) pp[i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * C::KPL);
+                float dl[16];
+                stat(dl, pdO, qb, 1.f);
+                f32x16 ds;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p;
+                    if constexpr (C::KPL == 8)
+                        p = (float)pp[r / 8][r % 8];
+                    else
+                        p = pp[r];
+                    ds[r] = p * (dp[r] - dl[r]);  // Eq. 17
+                }
+                frag sf[C::NI];
+                to_bfrag<T>(sf, ds);
+#pragma unroll
+                for (int db = 0; db < C::ND; ++db) {
+                    frag a[C::NI];
+                    tr.load(a, pQ, qb, db);
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], sf[i], acc[db]);  // Eq. 19
                 }
             }
         }
-        wait_lgkm0();
-        lds_barrier();  // P of every pair is in LDS
-        if (active) {
-            if (role == 0) {
-#pragma unroll
-                for (int qb = 0; qb < C::NQ2; ++qb) {
-                    dma.template issue_part<NP>(C::NQ2 + qb, nT, rs, pair);
-#pragma unroll
-                    for (int db = 0; db < C::ND; ++db) {
-                        frag a[C::NI];
-                        tr.load(a, tdO, qb, db);
-#pragma unroll
-                        for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], pf[qb][i], acc[db]);  // Eq. 15
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int qb = 0; qb < C::NQ2; ++qb) {
-                    dma.template issue_part<NP>(C::NQ2 + qb, nT, rs, pair);
-                    frag pr[C::NI];
-#pragma unroll
-                    for (int i = 0; i < C::NI; ++i)
-                        pr[i] = *reinterpret_cast<const typename M::frag *>(pbuf + qb * C::PBLK + i * C::KPL);
-                    float dl[16];
-                    stat(dl, tdO, qb, 1.f);
-                    f32x16 ds;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float p;
-                        if constexpr (C::KPL == 8)
-                            p = (float)pr[r / 8][r % 8];
-                        else
-                            p = pr[r];
-                        ds[r] = p * (dp[qb][r] - dl[r]);  // Eq. 17
-                    }
-                    frag sf[C::NI];
-                    to_bfrag<T>(sf, ds);
-#pragma unroll
-                    for (int db = 0; db < C::ND; ++db) {
-                        frag a[C::NI];
-                        tr.load(a, tQ, qb, db);
-#pragma unroll
-                        for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], sf[i], acc[db]);  // Eq. 19
-                    }
-                }
-            }
-        }
-        wait_lgkm0();  // this wave's reads of the stage and of P are complete
+        wait_lgkm0();  // this wave's reads of the stages and of P are complete
     };
-    for (int it = i0; it < nq2; it += 3) {
-        step(sQ0, sdO0, sQ2, sdO2, it);
-        if (it + 1 < nq2) step(sQ1, sdO1, sQ0, sdO0, it + 1);
-        if (it + 2 < nq2) step(sQ2, sdO2, sQ1, sdO1, it + 2);
+    // steps 0 .. ntile: step u finishes tile it-1 and starts tile it
+    for (int u = 0; u <= ntile; u += 3) {
+        step(sQ0, sQ2, sdO2, sQ1, sdO1, u);
+        if (u + 1 <= ntile) step(sQ1, sQ0, sdO0, sQ2, sdO2, u + 1);
+        if (u + 2 <= ntile) step(sQ2, sQ1, sdO1, sQ0, sdO0, u + 2);
     }
     wait_vmcnt<0>();
 
@@ -509,7 +514,7 @@ template <typename T, int D>
 static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                    const float *delta, void *dq, void *dk, void *dv, int BH, int S, float scale,
                    int causal, hipStream_t stream) {
-    using KC = KvTile<T, D, (sizeof(T) == 4 && D > 64) ? 32 : 64>;
+    using KC = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
     using QC = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
     const float c = scale * kLog2e;
     const long long g1 = (long long)((S + KC::BKV - 1) / KC::BKV) * BH;

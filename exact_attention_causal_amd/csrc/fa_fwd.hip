@@ -141,14 +141,21 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 dma.template issue_part<NP>(kb, nT, rs, hw);
-                frag kf[C::NSD];
-                load_row_frags<T, D>(kf, tK, kb * 32 + rsigma(l32), h);
+                // K fragments are read in groups of KG (each feeds NQB
+                // products): with two query blocks per wave the registers
+                // would not hold them all at once
+                constexpr int KG = NQB > 1 ? 2 : C::NSD;
+                const T *krow = tK + (kb * 32 + rsigma(l32)) * C::DMA::PD::PITCH + h * (D / 2);
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
-                    f32x16 t = f32x16{};
+                for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x16{};
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) t = M::run(kf[st], qf[qb][st], t);
-                    s[qb][kb] = t;
+                for (int g = 0; g < C::NSD / KG; ++g) {
+                    frag kf[KG];
+                    load_run<T, KG>(kf, krow + g * KG * C::KPL);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                        for (int st = 0; st < KG; ++st) s[qb][kb] = M::run(kf[st], qf[qb][g * KG + st], s[qb][kb]);
                 }
             }
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
@@ -264,6 +271,7 @@ static int fwd_for(const void *q, const void *k, const void *v, void *o, float *
                    float scale, int causal, hipStream_t stream) {
     // fp32 rows are twice the bytes: wide fp32 heads take 32-key tiles to fit three stages
     constexpr int BK = (sizeof(T) == 4 && D > 80) ? 32 : 64;
+    if constexpr (sizeof(T) == 2 && D == 128) return run_fwd<T, FwdTile<T, D, 2, 32, 8>>(q, k, v, o, lse, BH, S, scale, causal, stream);
     return run_fwd<T, FwdTile<T, D, 1, BK, 8>>(q, k, v, o, lse, BH, S, scale, causal, stream);
 }
 
