@@ -37,7 +37,7 @@ DEFAULT_WORKLOAD = "bf16_b1h16_s65536_d128"
 # rocprofv3 --pmc passes (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a
 # plain 1 GiB copy calibrates; see profiles/), keyed by a hash of the forward
 # kernel's sources: once those change, the figure is stale and reported as null.
-FWD_TRAFFIC = {"sources_sha1": "d954c3322dcff0870f76756c9dd99e49de707b47", "bytes": 9437324672}
+FWD_TRAFFIC = {"sources_sha1": "d2ee6b8d0f1c56cf259d0454306b08d2797f8f76", "bytes": 8331415200}
 FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp")
 
 
@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
                          "its HBM counters calibrate the traffic figures")
+    ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the --hold-entry entry point back to back for SECONDS "
+                         "(for sampling clocks and board power alongside) and exit")
+    ap.add_argument("--hold-entry", default="fwd", choices=("fwd", "bwd"))
     return ap.parse_args()
 
 
@@ -140,6 +144,20 @@ def main():
     def bwd():
         check(fa.fa_bwd(qd, kd, vd, dod, lse, delta, dq, dk, dv, ws, ws_bytes, B, H, S, D,
                         w.scale, 1, code, sh), "fa_bwd")
+
+    if args.hold > 0:
+        fwd(); pre(); bwd()
+        torch.cuda.synchronize()
+        f = fwd if args.hold_entry == "fwd" else bwd
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.hold:
+            for _ in range(5):
+                f()
+            torch.cuda.synchronize()
+            n += 5
+        print(json.dumps({"hold_entry": args.hold_entry, "calls": n,
+                          "ms_per_call": round((time.perf_counter() - t0) * 1e3 / n, 3)}), flush=True)
+        return
 
     log("warmup")
     for _ in range(args.warmup):

@@ -150,10 +150,14 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         load_run<T, C::NSD>(bf, (role ? v : k) + (size_t)key * D + h * (D / 2));
     else
         zero_run<T, C::NSD>(bf);
+    // The dS wave keeps V^T negated: its dP products start from D and yield
+    // D - dP, so dS = P o (dP - D) comes out negated with one multiply per
+    // element (the accumulated -dK^T is negated back at the store).
+    if (role) neg_run<T, C::NSD>(bf);
     TransReader<T, D> tr;
     tr.init(lane);
 
-    f32x16 acc[C::ND];  // dV^T (P wave) or dK^T (dS wave)
+    f32x16 acc[C::ND];  // dV^T (P wave) or -dK^T (dS wave)
 #pragma unroll
     for (int db = 0; db < C::ND; ++db) acc[db] = f32x16{};
 
@@ -273,19 +277,21 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
             // tile it-1: dP = dO V^T, dS = P o (dP - D), dK^T += Q^T dS
 #pragma unroll
             for (int qb = 0; qb < C::NQ2; ++qb) {
-                f32x16 dp = f32x16{};
+                float dl[16];
+                stat(dl, pdO, qb, 1.f);
+                f32x16 dp;  // D - dP (Eq. 16, with -V^T)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dp[r] = dl[r];
                 {
                     frag da[C::NSD];
                     load_row_frags<T, D>(da, pdO, qb * 32 + rsigma(l32), h);
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bf[st], dp);  // Eq. 16
+                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bf[st], dp);
                 }
                 frag pp[C::NI];
 #pragma unroll
                 for (int i = 0; i < C::NI; ++i) pp[i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * C::KPL);
-                float dl[16];
-                stat(dl, pdO, qb, 1.f);
-                f32x16 ds;
+                f32x16 ds;  // -dS (Eq. 17)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float p;
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                         p = (float)pp[r / 8][r % 8];
                     else
                         p = pp[r];
-                    ds[r] = p * (dp[r] - dl[r]);  // Eq. 17
+                    ds[r] = p * dp[r];
                 }
                 frag sf[C::NI];
                 to_bfrag<T>(sf, ds);
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 
     if (key < S) {
         T *out = role ? dk : dv;
-        const float mul = role ? scale : 1.f;
+        const float mul = role ? -scale : 1.f;
 #pragma unroll
         for (int db = 0; db < C::ND; ++db)
 #pragma unroll
@@ -395,6 +401,11 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
             dl[qb] = 0.f;
         }
     }
+    // dO^T is kept negated: the dP^T products then start from D and yield
+    // D - dP^T, so dS^T = P o (dP^T - D) comes out negated with one multiply
+    // per element (the accumulated -dQ^T is negated back at the store).
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) neg_run<T, C::NSD>(df[qb]);
     TransReader<T, D> tr;
     tr.init(lane);
 
@@ -437,7 +448,9 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
                     // S^T block: rows = keys j0 + 32*kb + ridx(r, h), col = query.
                     // (K and V fragments are not live at the same time: keeps two
                     // waves' worth of registers per SIMD)
-                    f32x16 s = f32x16{}, dp = f32x16{};
+                    f32x16 s = f32x16{}, dp;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dp[r] = dl[qb];
                     {
                         frag ka[C::NSD];
                         load_row_frags<T, D>(ka, tK, kb * 32 + rsigma(l32), h);
@@ -461,7 +474,7 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
                         for (int r = 0; r < 16; ++r) s[r] = (ridx(r, 0) < t) ? s[r] : 0.f;
                     }
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dl[qb]);  // Eq. 17
+                    for (int r = 0; r < 16; ++r) dp[r] = s[r] * dp[r];  // -dS^T (Eq. 17)
                     frag sf[C::NI];
                     to_bfrag<T>(sf, dp);
 #pragma unroll
@@ -492,7 +505,7 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
                 for (int hr = 0; hr < 2; ++hr) {
                     const int d0 = db * 32 + 16 * hr + 8 * h;
-                    if (d0 < D) store8<T>(dq + (size_t)qi * D + d0, acc[qb][db], 8 * hr, scale);
+                    if (d0 < D) store8<T>(dq + (size_t)qi * D + d0, acc[qb][db], 8 * hr, -scale);
                 }
         }
     }

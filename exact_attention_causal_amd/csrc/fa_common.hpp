@@ -105,6 +105,20 @@ __device__ inline void zero_run(typename Mma<T>::frag (&dst)[N]) {
     for (int i = 0; i < N; ++i) dst[i] = Mma<T>::zero();
 }
 
+// Negate fragments in place (sign flips only: exact).
+template <typename T, int N>
+__device__ inline void neg_run(typename Mma<T>::frag (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if constexpr (Mma<T>::KPL == 8) {
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            x[i] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x[i]) ^ 0x80008000u);
+        } else {
+            x[i] = -x[i];
+        }
+    }
+}
+
 // An fp32 output block (16 registers) as B-operand fragments (rounded to T).
 template <typename T>
 __device__ inline void to_bfrag(typename Mma<T>::frag (&dst)[16 / Mma<T>::KPL], const f32x16 &c) {
