@@ -200,12 +200,19 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
             }
         }
     };
-    // tile it holds queries this pair's keys depend on
-    auto active = [&](int it) {
-        return it >= i0 && it < nq2 && kw0 < S && !(causal && it * BQ2 + BQ2 - 1 < kw0);
-    };
     issue(sQ0, sdO0, i0);
-
+    // Step 0 has no tile before it: its "previous" stages get an empty range
+    // (the DMA lands zeros) and the P buffer it reads is cleared, so the
+    // lagged products of step 0 add exact zeros.  Every step then runs the
+    // same straight-line code (tiles a pair does not need are masked to P = 0),
+    // which lets the compiler interleave each wave's matrix and vector work.
+    issue(sQ2, sdO2, nq2);
+    {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 *z = reinterpret_cast<u32x4 *>(sP);
+        for (int i = tid; i < 2 * C::PBUF * (int)sizeof(T) / 16; i += C::NT) z[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    wait_lgkm0();
 
     // Step u (query tile it = i0 + u): stage tQ holds Q of tile it, pQ/pdO
     // hold tile it-1; nQ/ndO receive tile it+1 (the stages of tile it-2).
@@ -217,77 +224,81 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         // Tile it+1 is issued whole and unconditionally (see the forward
         // kernel); past the last tile its range is empty.
         issue(nQ, ndO, it + 1);
-        const bool cur = active(it), prev = active(it - 1);
         T *pw = sP + (u & 1) * C::PBUF + pair * C::NQ2 * C::PBLK + lane * 16;        // P of tile it
         const T *pr = sP + ((u + 1) & 1) * C::PBUF + pair * C::NQ2 * C::PBLK + lane * 16;  // P of it-1
         if (role == 0) {
-            if (prev) {
-                // dV^T += dO^T P for tile it-1, P read back from the buffer
-                // this wave wrote in the previous step
+            // dV^T += dO^T P for tile it-1 (P read back from the buffer this
+            // wave wrote in the previous step), and S, P of tile it
+            frag pp[C::NQ2][C::NI];
 #pragma unroll
-                for (int qb = 0; qb < C::NQ2; ++qb) {
-                    frag pp[C::NI];
+            for (int qb = 0; qb < C::NQ2; ++qb)
 #pragma unroll
-                    for (int i = 0; i < C::NI; ++i)
-                        pp[i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * C::KPL);
+                for (int i = 0; i < C::NI; ++i) pp[qb][i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * C::KPL);
+            f32x16 s[C::NQ2];
 #pragma unroll
-                    for (int db = 0; db < C::ND; ++db) {
-                        frag a[C::NI];
-                        tr.load(a, pdO, qb, db);
+            for (int qb = 0; qb < C::NQ2; ++qb) {
+                // S block: rows = queries q0 + 32*qb + ridx(r, h), col = key.
+                s[qb] = f32x16{};
+                frag qa[C::NSD];
+                load_row_frags<T, D>(qa, tQ, qb * 32 + rsigma(l32), h);
 #pragma unroll
-                        for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], pp[i], acc[db]);  // Eq. 15
-                    }
-                }
+                for (int st = 0; st < C::NSD; ++st) s[qb] = M::run(qa[st], bf[st], s[qb]);
             }
-            if (cur) {
-                const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
+#pragma unroll
+            for (int qb = 0; qb < C::NQ2; ++qb) {
+                float lv[16];
+                stat(lv, tQ, qb, kLog2e);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[qb][r] = fast_exp2(fmaf(s[qb][r], c, -lv[r]));  // Eq. 14
+            }
+#pragma unroll
+            for (int qb = 0; qb < C::NQ2; ++qb)
+#pragma unroll
+                for (int db = 0; db < C::ND; ++db) {
+                    frag a[C::NI];
+                    tr.load(a, pdO, qb, db);
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], pp[qb][i], acc[db]);  // Eq. 15
+                }
+            const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
+            if (need_mask) {
+                asm volatile("");  // a real branch: only diagonal / tail tiles pay for masking
+                // query q0 + 32*qb + ridx(r, h) is kept iff it is at least `lo` and below `hi`
 #pragma unroll
                 for (int qb = 0; qb < C::NQ2; ++qb) {
-                    // S block: rows = queries q0 + 32*qb + ridx(r, h), col = key.
-                    f32x16 s = f32x16{};
-                    {
-                        frag qa[C::NSD];
-                        load_row_frags<T, D>(qa, tQ, qb * 32 + rsigma(l32), h);
-#pragma unroll
-                        for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], bf[st], s);
-                    }
-                    float lv[16];
-                    stat(lv, tQ, qb, kLog2e);
-                    // query q0 + 32*qb + ridx(r, h) is kept iff it is at least `lo` and below `hi`
                     const int lo = (causal ? key : 0) - q0 - 32 * qb - 2 * h;
                     const int hi = S - q0 - 32 * qb - 2 * h;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
-                    if (need_mask) {
-                        asm volatile("");  // a real branch: only diagonal / tail tiles pay for masking
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int e = ridx(r, 0);
-                            s[r] = (e >= lo && e < hi) ? s[r] : 0.f;
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int e = ridx(r, 0);
+                        s[qb][r] = (e >= lo && e < hi) ? s[qb][r] : 0.f;
                     }
-                    frag pf[C::NI];
-                    to_bfrag<T>(pf, s);
-                    // hand P to the partner (same lane layout on both sides)
-#pragma unroll
-                    for (int i = 0; i < C::NI; ++i) *reinterpret_cast<frag *>(pw + qb * C::PBLK + i * C::KPL) = pf[i];
                 }
             }
-        } else if (prev) {
+            // hand P to the partner (same lane layout on both sides)
+#pragma unroll
+            for (int qb = 0; qb < C::NQ2; ++qb) {
+                frag pf[C::NI];
+                to_bfrag<T>(pf, s[qb]);
+#pragma unroll
+                for (int i = 0; i < C::NI; ++i) *reinterpret_cast<frag *>(pw + qb * C::PBLK + i * C::KPL) = pf[i];
+            }
+        } else {
             // tile it-1: dP = dO V^T, dS = P o (dP - D), dK^T += Q^T dS
+            f32x16 dp[C::NQ2];  // D - dP (Eq. 16, with -V^T)
 #pragma unroll
             for (int qb = 0; qb < C::NQ2; ++qb) {
                 float dl[16];
                 stat(dl, pdO, qb, 1.f);
-                f32x16 dp;  // D - dP (Eq. 16, with -V^T)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dp[r] = dl[r];
-                {
-                    frag da[C::NSD];
-                    load_row_frags<T, D>(da, pdO, qb * 32 + rsigma(l32), h);
+                for (int r = 0; r < 16; ++r) dp[qb][r] = dl[r];
+                frag da[C::NSD];
+                load_row_frags<T, D>(da, pdO, qb * 32 + rsigma(l32), h);
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bf[st], dp);
-                }
+                for (int st = 0; st < C::NSD; ++st) dp[qb] = M::run(da[st], bf[st], dp[qb]);
+            }
+#pragma unroll
+            for (int qb = 0; qb < C::NQ2; ++qb) {
                 frag pp[C::NI];
 #pragma unroll
                 for (int i = 0; i < C::NI; ++i) pp[i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * C::KPL);
@@ -299,7 +310,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                         p = (float)pp[r / 8][r % 8];
                     else
                         p = pp[r];
-                    ds[r] = p * dp[r];
+                    ds[r] = p * dp[qb][r];
                 }
                 frag sf[C::NI];
                 to_bfrag<T>(sf, ds);
