@@ -142,21 +142,25 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
             for (int kb = 0; kb < C::NKB; ++kb) {
                 dma.template issue_part<NP>(kb, nT, rs, hw);
                 // K fragments are read in groups of KG (each feeds NQB
-                // products): with two query blocks per wave the registers
-                // would not hold them all at once
+                // products; an odd count ends with a single one): with two
+                // query blocks per wave the registers would not hold them all
                 constexpr int KG = NQB > 1 ? 2 : C::NSD;
                 const T *krow = tK + (kb * 32 + rsigma(l32)) * C::DMA::PD::PITCH + h * (D / 2);
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x16{};
-#pragma unroll
-                for (int g = 0; g < C::NSD / KG; ++g) {
-                    frag kf[KG];
-                    load_run<T, KG>(kf, krow + g * KG * C::KPL);
+                auto group = [&](auto n, int f0) {
+                    constexpr int N = decltype(n)::value;
+                    frag kf[N];
+                    load_run<T, N>(kf, krow + f0 * C::KPL);
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-                        for (int st = 0; st < KG; ++st) s[qb][kb] = M::run(kf[st], qf[qb][g * KG + st], s[qb][kb]);
-                }
+                        for (int st = 0; st < N; ++st) s[qb][kb] = M::run(kf[st], qf[qb][f0 + st], s[qb][kb]);
+                };
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x16{};
+#pragma unroll
+                for (int g = 0; g < C::NSD / KG; ++g) group(std::integral_constant<int, KG>{}, g * KG);
+                if constexpr (C::NSD % KG != 0)
+                    group(std::integral_constant<int, C::NSD % KG>{}, C::NSD / KG * KG);
             }
             const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
             if (need_mask) {
@@ -271,7 +275,15 @@ static int fwd_for(const void *q, const void *k, const void *v, void *o, float *
                    float scale, int causal, hipStream_t stream) {
     // fp32 rows are twice the bytes: wide fp32 heads take 32-key tiles to fit three stages
     constexpr int BK = (sizeof(T) == 4 && D > 80) ? 32 : 64;
-    if constexpr (sizeof(T) == 2 && D == 128) return run_fwd<T, FwdTile<T, D, 2, 32, 8>>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    // bf16 D=128: 64 queries per wave over 32-key tiles halves the K/V reads
+    // per FLOP, but makes the query tiles twice as long; keep it for problems
+    // with at least four such tiles per CU (short causal problems lose more
+    // to the uneven tile lengths than they gain).  Measured slower at D=80.
+    using C2 = FwdTile<T, D, 2, 32, 8>;
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        const long long tiles2 = (long long)((S + C2::BQ - 1) / C2::BQ) * BH;
+        if (tiles2 >= 4 * kNumCU) return run_fwd<T, C2>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    }
     return run_fwd<T, FwdTile<T, D, 1, BK, 8>>(q, k, v, o, lse, BH, S, scale, causal, stream);
 }
 
