@@ -15,6 +15,7 @@ times the fp64 CPU oracle on a bounded slice of the same workload.
 """
 import argparse
 import json
+import statistics
 import math
 import os
 import sys
@@ -53,8 +54,8 @@ def fwd_sources_sha1():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=12288,
@@ -179,9 +180,13 @@ def main():
         ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_fwd = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    t_pre = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    t_bwd = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    per_fwd = [e[0].elapsed_time(e[1]) for e in ev]
+    per_pre = [e[1].elapsed_time(e[2]) for e in ev]
+    per_bwd = [e[2].elapsed_time(e[3]) for e in ev]
+    per_step = [e[0].elapsed_time(e[3]) for e in ev]
+    t_fwd = sum(per_fwd) / args.steps
+    t_pre = sum(per_pre) / args.steps
+    t_bwd = sum(per_bwd) / args.steps
     ms_step = wall * 1e3 / args.steps
 
     pairs = w.causal_pairs()
@@ -212,6 +217,9 @@ def main():
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_of_peak": round(fwd_tf / peak, 4),
         "ms": {"fwd": round(t_fwd, 4), "bwd_preprocess": round(t_pre, 4), "bwd": round(t_bwd, 4)},
+        "ms_event_stats": {n: {"median": round(statistics.median(x), 4), "min": round(min(x), 4),
+                               "max": round(max(x), 4)}
+                           for n, x in (("step", per_step), ("fwd", per_fwd), ("bwd", per_bwd))},
         "roofline": {"kernel": "fwd_kernel (fa_fwd)", "bound": "mfma", "achieved": round(fwd_tf, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tf / peak, 4),
                      "traffic": (FWD_TRAFFIC["bytes"] if w.name == DEFAULT_WORKLOAD
