@@ -67,6 +67,10 @@ def parse():
                     help="only run the --hold-entry entry point back to back for SECONDS "
                          "(for sampling clocks and board power alongside) and exit")
     ap.add_argument("--hold-entry", default="fwd", choices=("fwd", "bwd"))
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time the benchmark sweep (B=1, H=1, S = 128 .. 65536 in powers of "
+                         "two, D in 16/32/64/128, bf16 and fp32, causal and not), print a "
+                         "markdown table and exit")
     return ap.parse_args()
 
 
@@ -95,6 +99,69 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def sweep(dev):
+    """Latency sweep over the grid of the handout's FlashAttention-2 benchmark.
+
+    One head (B=1, H=1) per point, as in that benchmark; times are medians of
+    HIP-event times over repeated calls after warm-up.  fwd = fa_fwd;
+    fwd+bwd = fa_fwd + fa_bwd_preprocess + fa_bwd.
+    """
+    from exact_attention_causal_amd.inputs import make_inputs
+    fa.load_library()
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    rows = []
+    print("| dtype | causal | D | S | fwd ms | fwd+bwd ms | fwd TFLOP/s | fwd+bwd TFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|")
+    for dtype in ("bf16", "f32"):
+        code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
+        for causal in (1, 0):
+            for D in (16, 32, 64, 128):
+                for e in range(7, 17):
+                    S = 1 << e
+                    q, k, v, do = (x.to(dev) for x in make_inputs(1, 1, S, D, dtype, seed=e))
+                    o = torch.empty_like(q)
+                    lse = torch.empty((1, 1, S), device=dev, dtype=torch.float32)
+                    delta = torch.empty_like(lse)
+                    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                    scale = 1.0 / math.sqrt(D)
+
+                    def fwd():
+                        rc = fa.fa_fwd(q, k, v, o, lse, 1, 1, S, D, scale, causal, code, sh)
+                        assert rc == 0, fa.fa_strerror(rc)
+
+                    def step():
+                        fwd()
+                        rc = fa.fa_bwd_preprocess(o, do, delta, 1, 1, S, D, code, sh)
+                        assert rc == 0, fa.fa_strerror(rc)
+                        rc = fa.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, None, 0, 1, 1, S, D,
+                                       scale, causal, code, sh)
+                        assert rc == 0, fa.fa_strerror(rc)
+
+                    def timed(f, n):
+                        for _ in range(3):
+                            f()
+                        ts = []
+                        for _ in range(n):
+                            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                            a.record(stream)
+                            f()
+                            b.record(stream)
+                            ts.append((a, b))
+                        torch.cuda.synchronize()
+                        return statistics.median(x.elapsed_time(y) for x, y in ts)
+
+                    n = 10 if S >= 16384 else 30
+                    t_f, t_s = timed(fwd, n), timed(step, n)
+                    pairs = S * (S + 1) // 2 if causal else S * S
+                    tf_f = 4 * D * pairs / (t_f * 1e-3) / 1e12
+                    tf_s = 14 * D * pairs / (t_s * 1e-3) / 1e12
+                    rows.append(dict(dtype=dtype, causal=causal, D=D, S=S, fwd_ms=t_f, step_ms=t_s))
+                    print(f"| {dtype} | {causal} | {D} | {S} | {t_f:.4f} | {t_s:.4f} | {tf_f:.1f} | "
+                          f"{tf_s:.1f} |", flush=True)
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -114,6 +181,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.sweep:
+        sweep(dev)
         return
     w = WORKLOADS[args.workload]
     fa.load_library()

@@ -169,3 +169,40 @@ def backward(q, k, v, o, lse, dout, causal=True, scale=None, delta=None, grads=N
     _check(fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, ws_bytes, B, H, S, D, scale,
                   causal, code, stream), "fa_bwd")
     return dq, dk, dv, delta
+
+
+# ------------------------------------------------------------- autograd ---
+
+class FlashAttention(torch.autograd.Function):
+    """Attention as a differentiable op (CS336 Assignment 2 handout, section 4.2.2 (a)).
+
+    forward(q, k, v, is_causal=False, scale=None) returns O and keeps only
+    q, k, v, O and the logsumexp L for the backward, which recomputes P from L
+    (handout Algorithm 2).  Inputs are [B, H, S, D] or [B, S, D] (one head)
+    bf16 or fp32 GPU tensors; the default scale is 1/sqrt(D).
+    """
+
+    @staticmethod
+    def forward(ctx, q, k, v, is_causal=False, scale=None):
+        three = q.dim() == 3
+        if three:
+            q, k, v = (x.unsqueeze(1) for x in (q, k, v))
+        o, lse = forward(q, k, v, causal=bool(is_causal), scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.is_causal, ctx.scale, ctx.three = bool(is_causal), scale, three
+        return o.squeeze(1) if three else o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        if ctx.three:
+            do = do.unsqueeze(1)
+        dq, dk, dv, _ = backward(q, k, v, o, lse, do, causal=ctx.is_causal, scale=ctx.scale)
+        if ctx.three:
+            dq, dk, dv = (x.squeeze(1) for x in (dq, dk, dv))
+        return dq, dk, dv, None, None
+
+
+def flash_attention(q, k, v, is_causal=False, scale=None):
+    """Differentiable attention through the HIP kernels (see FlashAttention)."""
+    return FlashAttention.apply(q, k, v, is_causal, scale)

@@ -208,6 +208,35 @@ def test_noncausal(S, D, dtype):
     check_full(q, k, v, do, dtype, causal=False, label=f"noncausal S={S} D={D}")
 
 
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("f32", False)])
+def test_autograd_function(dtype, causal):
+    # the differentiable op: gradients of sum(W * O) equal the oracle's dQ, dK, dV for dO = W
+    q, k, v, w = make_inputs(2, 3, 150, 64, dtype, seed=500)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev).requires_grad_(True) for x in (q, k, v))
+    o = fa.flash_attention(qd, kd, vd, is_causal=causal)
+    (o.float() * w.to(dev).float()).sum().backward()
+    torch.cuda.synchronize()
+    r = oracle.backward(*(x.double().numpy() for x in (q, k, v, w)), causal=causal)
+    tol = TOL[dtype]
+    assert rel(o.detach().double().cpu().numpy(), r["o"]) <= tol["o"]
+    for n, t in (("dq", qd), ("dk", kd), ("dv", vd)):
+        assert rel(t.grad.double().cpu().numpy(), r[n]) <= tol["grad"], n
+
+
+def test_autograd_function_single_head_layout():
+    # [B, S, D] inputs (no head axis) are one head each
+    q, k, v, w = make_inputs(3, 1, 77, 32, "bf16", seed=501)
+    dev = torch.device("cuda:0")
+    q3, k3, v3 = (x[:, 0].to(dev).requires_grad_(True) for x in (q, k, v))
+    o = fa.flash_attention(q3, k3, v3, is_causal=True)
+    assert o.shape == q3.shape
+    (o.float() * w[:, 0].to(dev).float()).sum().backward()
+    r = oracle.backward(*(x.double().numpy() for x in (q, k, v, w)), causal=True)
+    assert rel(o.detach().double().cpu().numpy(), r["o"][:, 0]) <= TOL["bf16"]["o"]
+    assert rel(q3.grad.double().cpu().numpy(), r["dq"][:, 0]) <= TOL["bf16"]["grad"]
+
+
 def test_custom_scale_and_peaky_scores():
     q, k, v, do = make_inputs(1, 2, 257, 64, "bf16", seed=7, qk_mult=3.0)
     check_full(q, k, v, do, "bf16", causal=True, scale=0.3, label="scale=0.3 peaky")
