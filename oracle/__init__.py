@@ -37,8 +37,10 @@ def _load():
     lib.oracle_head_stats.argtypes = [_dp] * 6 + [_L, _L, _D, _I, _I]
     lib.oracle_rows.argtypes = [_dp, _dp, _dp, _dp, _lp, _L, _dp, _dp, _dp, _L, _L, _D, _I, _I]
     lib.oracle_cols.argtypes = [_dp] * 6 + [_lp, _L, _dp, _dp, _L, _L, _D, _I, _I]
+    lib.oracle_fwd_offset.argtypes = [_dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L, _D, _I, _L, _I]
+    lib.oracle_merge.argtypes = [_dp, _dp, _L, _dp, _dp, _L, _L]
     for f in (lib.oracle_fwd, lib.oracle_bwd, lib.oracle_probs, lib.oracle_head_stats,
-              lib.oracle_rows, lib.oracle_cols):
+              lib.oracle_rows, lib.oracle_cols, lib.oracle_fwd_offset, lib.oracle_merge):
         f.restype = None
     _lib = lib
     return lib
@@ -74,6 +76,40 @@ def forward(q, k, v, scale=None, causal=True, nthreads=0):
     lib.oracle_fwd(_ptr(qh), _ptr(kh), _ptr(vh), _ptr(o), _ptr(lse), BH, Sq, Sk, D,
                    float(scale), int(bool(causal)), int(nthreads))
     return o.reshape(qshape), lse.reshape(qshape[:-1])
+
+
+def forward_offset(q, k, v, q_offset=0, scale=None, causal=True, nthreads=0):
+    """O, L for [..., Sq, D] queries against [..., Sk, D] keys, query i placed
+    q_offset positions after key 0 (causal: key j allowed iff j <= i + q_offset).
+    Rows with no allowed key give O = 0, L = -inf."""
+    lib = _load()
+    qh, qshape = _heads(q)
+    kh, _ = _heads(k)
+    vh, _ = _heads(v)
+    BH, Sq, D = qh.shape
+    Sk = kh.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.empty_like(qh)
+    lse = np.empty((BH, Sq), dtype=np.float64)
+    lib.oracle_fwd_offset(_ptr(qh), _ptr(kh), _ptr(vh), _ptr(o), _ptr(lse), BH, Sq, Sk, D,
+                          float(scale), int(bool(causal)), int(q_offset), int(nthreads))
+    return o.reshape(qshape), lse.reshape(qshape[:-1])
+
+
+def merge(o_parts, lse_parts):
+    """Merge results over disjoint key sets: o_parts [n, ..., S, D], lse_parts [n, ..., S]."""
+    lib = _load()
+    op = _f64(o_parts)
+    lp = _f64(lse_parts)
+    n = op.shape[0]
+    D = op.shape[-1]
+    rows = int(np.prod(op.shape[1:-1])) if op.ndim > 2 else 1
+    assert lp.shape == op.shape[:-1]
+    o = np.empty(op.shape[1:])
+    lse = np.empty(lp.shape[1:])
+    lib.oracle_merge(_ptr(op), _ptr(lp), n, _ptr(o), _ptr(lse), rows, D)
+    return o, lse
 
 
 def backward(q, k, v, dout, scale=None, causal=True, nthreads=0):

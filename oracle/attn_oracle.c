@@ -296,3 +296,91 @@ void oracle_cols(const double *q, const double *k, const double *v, const double
         }
     }
 }
+
+
+/*
+ * Forward with the queries shifted against the keys (queries and keys of
+ * different lengths, e.g. one shard of a sequence against another):
+ * query i sits q_offset positions after key 0, so under the causal mask key j
+ * is allowed iff j <= i + q_offset.  A row that allows no key has no softmax;
+ * it gets O_i = 0 and L_i = -inf (the empty sum), the values that leave any
+ * merge with other key sets unchanged.  Same equations as oracle_fwd
+ * (handout Eq. 4-6, 12).
+ */
+void oracle_fwd_offset(const double *q, const double *k, const double *v,
+                       double *o, double *lse, long BH, long Sq, long Sk, long D,
+                       double scale, int causal, long q_offset, int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+#pragma omp for collapse(2) schedule(dynamic, 16)
+        for (long h = 0; h < BH; ++h)
+            for (long i = 0; i < Sq; ++i) {
+                const double *qh = q + h * Sq * D, *kh = k + h * Sk * D, *vh = v + h * Sk * D;
+                long nkeys = Sk;
+                if (causal) {
+                    nkeys = i + 1 + q_offset;
+                    if (nkeys < 0)
+                        nkeys = 0;
+                    if (nkeys > Sk)
+                        nkeys = Sk;
+                }
+                double *oi = o + (h * Sq + i) * D;
+                if (nkeys == 0) {
+                    for (long d = 0; d < D; ++d)
+                        oi[d] = 0.0;
+                    lse[h * Sq + i] = -INFINITY;
+                    continue;
+                }
+                row_forward(qh + i * D, kh, vh, Sk, D, scale, nkeys, p, oi, lse + h * Sq + i);
+            }
+        free(p);
+    }
+}
+
+/*
+ * Merge of attention results over disjoint key sets (the ring-attention
+ * blog "[Attention]FlashAttention/Ring-Attention/混合序列并行的统一原理",
+ * section "online attention": the softmax numerators and denominators of
+ * the two halves are rescaled to the common maximum and added).  With each
+ * part's result given as its normalised output o_r and logsumexp L_r
+ * (denominator B_r e^{m_r} = e^{L_r}), the merged row is
+ *   M = max_r L_r,  w_r = e^{L_r - M},  O = sum_r w_r o_r / sum_r w_r,
+ *   L = M + ln sum_r w_r,
+ * and a row that is empty in every part stays O = 0, L = -inf.
+ * o_parts [n][rows][D], lse_parts [n][rows]; o [rows][D], lse [rows].
+ */
+void oracle_merge(const double *o_parts, const double *lse_parts, long n, double *o,
+                  double *lse, long rows, long D)
+{
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < rows; ++i) {
+        double M = -INFINITY;
+        for (long r = 0; r < n; ++r)
+            if (lse_parts[r * rows + i] > M)
+                M = lse_parts[r * rows + i];
+        double *oi = o + i * D;
+        for (long d = 0; d < D; ++d)
+            oi[d] = 0.0;
+        if (M == -INFINITY) {
+            lse[i] = -INFINITY;
+            continue;
+        }
+        double wsum = 0.0;
+        for (long r = 0; r < n; ++r) {
+            const double w = exp(lse_parts[r * rows + i] - M);
+            wsum += w;
+            const double *pr = o_parts + (r * rows + i) * D;
+            for (long d = 0; d < D; ++d)
+                oi[d] += w * pr[d];
+        }
+        for (long d = 0; d < D; ++d)
+            oi[d] /= wsum;
+        lse[i] = M + log(wsum);
+    }
+}

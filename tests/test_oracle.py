@@ -208,6 +208,85 @@ def test_split_kv_merge_causal():
     np.testing.assert_allclose(l0, lse[:, :s], atol=1e-14)
 
 
+# ------------------------------------- shifted queries and the n-way merge ---
+
+def _torch_shifted(q, k, v, q_offset, causal, scale):
+    """fp64 torch attention with an explicitly built shifted causal mask."""
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    s = (qt @ kt.transpose(-1, -2)) * scale
+    Sq, Sk = q.shape[-2], k.shape[-2]
+    if causal:
+        i = torch.arange(Sq)[:, None]
+        j = torch.arange(Sk)[None, :]
+        s = s.masked_fill(j > i + q_offset, float("-inf"))
+    return (torch.softmax(s, -1) @ vt).numpy(), torch.logsumexp(s, -1).numpy()
+
+
+@pytest.mark.parametrize("Sq,Sk,off", [(7, 11, 0), (7, 11, 4), (9, 6, -3), (5, 8, 20), (6, 6, -6)])
+def test_shifted_forward_matches_torch_with_explicit_mask(Sq, Sk, off):
+    D = 5
+    q, k, v = _rand((2, Sq, D), 70), _rand((2, Sk, D), 71), _rand((2, Sk, D), 72)
+    sc = 1 / math.sqrt(D)
+    o, lse = oracle.forward_offset(q, k, v, q_offset=off, scale=sc, causal=True)
+    ot, lt = _torch_shifted(q, k, v, off, True, sc)
+    empty = np.arange(Sq) + off < 0          # rows that allow no key
+    np.testing.assert_allclose(o[:, ~empty], ot[:, ~empty], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[:, ~empty], lt[:, ~empty], rtol=0, atol=1e-12)
+    assert np.all(o[:, empty] == 0.0) and np.all(np.isneginf(lse[:, empty]))
+    # offset 0 with equal lengths is the plain causal forward; without the mask nothing shifts
+    if Sq == Sk and off == 0:
+        o0, l0 = oracle.forward(q, k, v, scale=sc, causal=True)
+        np.testing.assert_array_equal(o, o0)
+    on, ln = oracle.forward_offset(q, k, v, q_offset=off, scale=sc, causal=False)
+    of, lf = oracle.forward(q, k, v, scale=sc, causal=False)
+    np.testing.assert_array_equal(on, of)
+    np.testing.assert_array_equal(ln, lf)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_nway_merge_of_key_chunks_is_full_attention(causal):
+    """Three key chunks at their positions, merged, equal attention over all keys."""
+    Sq, Sk, D, q_pos = 12, 17, 4, 5           # query i sits at position q_pos + i
+    q, k, v = _rand((3, Sq, D), 80), _rand((3, Sk, D), 81), _rand((3, Sk, D), 82)
+    sc = 1 / math.sqrt(D)
+    o, lse = oracle.forward_offset(q, k, v, q_offset=q_pos, scale=sc, causal=causal)
+    bounds = [0, 6, 13, Sk]
+    parts = [oracle.forward_offset(q, k[:, a:b], v[:, a:b], q_offset=q_pos - a, scale=sc,
+                                   causal=causal) for a, b in zip(bounds[:-1], bounds[1:])]
+    om, lm = oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    np.testing.assert_allclose(om, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lm, lse, rtol=0, atol=1e-12)
+    ot, lt = _torch_shifted(q, k, v, q_pos, causal, sc)
+    np.testing.assert_allclose(om, ot, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lm, lt, rtol=0, atol=1e-12)
+
+
+def test_merge_closed_forms():
+    o1, l1 = _rand((2, 5, 3), 90), _rand((2, 5), 91)
+    # one part: unchanged
+    om, lm = oracle.merge(o1[None], l1[None])
+    np.testing.assert_allclose(om, o1, atol=1e-15)
+    np.testing.assert_allclose(lm, l1, atol=1e-15)
+    # an empty part (O = 0, L = -inf) changes nothing
+    empty_o, empty_l = np.zeros_like(o1), np.full_like(l1, -np.inf)
+    om, lm = oracle.merge(np.stack([o1, empty_o]), np.stack([l1, empty_l]))
+    np.testing.assert_allclose(om, o1, atol=1e-15)
+    np.testing.assert_allclose(lm, l1, atol=1e-15)
+    # the same part twice: same output, L + ln 2
+    om, lm = oracle.merge(np.stack([o1, o1]), np.stack([l1, l1]))
+    np.testing.assert_allclose(om, o1, atol=1e-14)
+    np.testing.assert_allclose(lm, l1 + math.log(2.0), atol=1e-14)
+    # all parts empty: the row stays empty
+    om, lm = oracle.merge(np.stack([empty_o, empty_o]), np.stack([empty_l, empty_l]))
+    assert np.all(om == 0.0) and np.all(np.isneginf(lm))
+    # agrees with the two-block rule written above for two parts
+    o2, l2 = _rand((2, 5, 3), 92), _rand((2, 5), 93)
+    om, lm = oracle.merge(np.stack([o1, o2]), np.stack([l1, l2]))
+    ref_o, ref_l = _merge(o1, l1, o2, l2)
+    np.testing.assert_allclose(om, ref_o, atol=1e-14)
+    np.testing.assert_allclose(lm, ref_l, atol=1e-14)
+
+
 # ---------------------------------------- library routine (torch fp64 CPU) ---
 
 @pytest.mark.parametrize("S,D,causal,mult", [(33, 16, True, 1.0), (64, 8, True, 3.0),
