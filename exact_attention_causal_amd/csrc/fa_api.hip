@@ -85,6 +85,42 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const 
         fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv, B * H, S, D, scale, causal, stream));
 }
 
+int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, float *lse_parts,
+                   int B, int H, int Sq, int Sk, int D, float scale, int causal, int q_offset,
+                   int n_split, fa_dtype dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o_parts || !lse_parts) return FA_EINVAL;
+    if (causal != 0 && causal != 1) return FA_EINVAL;
+    if (n_split < 1 || n_split > 65535) return FA_EINVAL;
+    if (int rc = check_scale(scale)) return rc;
+    if (int rc = check_shape(B, H, Sq, D, dtype)) return rc;
+    if (int rc = check_shape(B, H, Sk, D, dtype)) return rc;
+    if (Sq > (1 << 30) || Sk > (1 << 30)) return FA_EINVAL;  // positions stay within int
+    // n_split copies of the output must still be addressable
+    const long long per_split = (long long)B * H * Sq * D;
+    if (per_split > 0x3fffffffffffffffLL / n_split) return FA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_parts) || !aligned16(lse_parts))
+        return FA_EALIGN;
+    const long long per = ((long long)Sk + 64LL * n_split - 1) / (64LL * n_split);
+    const long long chunk = 64 * per;
+    if (chunk * n_split > 0x7fffffffLL) return FA_EINVAL;
+    // offsets beyond [-Sq, Sk] change nothing (every key allowed / none)
+    const int off = (int)(q_offset < -Sq ? -Sq : (q_offset > Sk ? Sk : q_offset));
+    return map_launch(fa::launch_fwd_partial(dtype, q, k, v, o_parts, lse_parts, B * H, Sq, Sk, D, scale,
+                                             causal, off, n_split, (int)chunk, stream));
+}
+
+int fa_merge(const float *o_parts, const float *lse_parts, int n_parts, void *o, float *lse, int B,
+             int H, int S, int D, fa_dtype dtype, hipStream_t stream) {
+    if (!o_parts || !lse_parts || !o || !lse) return FA_EINVAL;
+    if (n_parts < 1) return FA_EINVAL;
+    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
+    const long long per_part = (long long)B * H * S * D;
+    if (per_part > 0x3fffffffffffffffLL / n_parts) return FA_EINVAL;
+    if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return FA_EALIGN;
+    return map_launch(fa::launch_merge(dtype, o_parts, lse_parts, n_parts, o, lse, (long long)B * H * S, D,
+                                       stream));
+}
+
 const char *fa_strerror(int status) {
     switch (status) {
     case FA_OK: return "success";

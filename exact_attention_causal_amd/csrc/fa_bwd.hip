@@ -453,7 +453,7 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 __builtin_amdgcn_sched_barrier(0);
-                dma.template issue_part<C::NKB>(kb, nT, rs, hw);
+                dma.issue_part(kb, C::NKB, nT, rs, hw);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     // S^T block: rows = keys j0 + 32*kb + ridx(r, h), col = query.

@@ -206,10 +206,12 @@ struct TileDma {
         T *dst = lds + (wave * IPW + i) * (1024 / (int)sizeof(T));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff[i], 0, 0, 0);
     }
-    // Issue part p of NP near-equal parts of this wave's share.
-    template <int NP>
-    __device__ inline void issue_part(int p, T *lds, __amdgpu_buffer_rsrc_t rs, int wave) const {
-        const int a = (IPW * p + NP - 1) / NP, b = (IPW * (p + 1) + NP - 1) / NP;
+    // Issue part p of np near-equal parts of this wave's share (np is a
+    // compile-time constant at every call; it is a plain argument because a
+    // member template taking the descriptor type does not substitute in the
+    // host compilation pass).
+    __device__ inline void issue_part(int p, int np, T *lds, __amdgpu_buffer_rsrc_t rs, int wave) const {
+        const int a = (IPW * p + np - 1) / np, b = (IPW * (p + 1) + np - 1) / np;
 #pragma unroll
         for (int i = 0; i < IPW; ++i)
             if (i >= a && i < b) issue_one(i, lds, rs, wave);

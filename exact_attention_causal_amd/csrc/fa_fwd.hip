@@ -54,11 +54,24 @@ struct FwdTile {
 // hold exactly as well as values <= 1, and O and l keep the same stale m.
 constexpr float kRescaleSlack = 8.f;
 
-template <typename T, typename C>
+// Problem shape of one launch.  Query i of a head sits `off` positions after
+// key 0, so the causal mask allows key j iff j <= i + off (off = 0 and
+// Sq = Sk for self-attention).  The keys may be split into chunks of `chunk`
+// rows, one per blockIdx.y, each producing its own normalised O and L over
+// its keys (outputs `o_split` / `l_split` elements apart).
+struct FwdShape {
+    int BH, Sq, Sk, off, chunk, causal, nqt;
+    float c;  // scale * log2(e)
+    long long o_split, l_split;
+};
+
+// GEN = false is self-attention (no shift, one chunk of all keys): the shift
+// is then a compile-time zero, which the register allocator needs to keep the
+// 64-queries-per-wave tile within 256 registers.
+template <typename T, typename C, typename OutT, bool GEN>
 __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                    const T *__restrict__ v, T *__restrict__ o,
-                                                    float *__restrict__ lse, int BH, int S, float c,
-                                                    int causal, int nqt) {
+                                                    const T *__restrict__ v, OutT *__restrict__ o,
+                                                    float *__restrict__ lse, FwdShape a) {
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
@@ -72,15 +85,23 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
+    const int BH = a.BH, S = a.Sq, causal = a.causal;
+    const float c = a.c;
     const int bid = blockIdx.x;
-    const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
+    const int qt = causal ? (a.nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
-    const size_t hoff = (size_t)bh * S * D;
-    q += hoff;
-    k += hoff;
-    v += hoff;
-    o += hoff;
-    lse += (size_t)bh * S;
+    // this launch's keys: chunk blockIdx.y of the head's key rows
+    const int kbeg = GEN ? blockIdx.y * a.chunk : 0;
+    // (readfirstlane keeps these wave-uniform in scalar registers: the clamp
+    // is selected as vector min/max, which would make every branch on them
+    // look divergent)
+    const int Sk = GEN ? __builtin_amdgcn_readfirstlane(max(0, min(a.chunk, a.Sk - kbeg))) : S;
+    const int off = GEN ? __builtin_amdgcn_readfirstlane(a.off - kbeg) : 0;
+    q += (size_t)bh * S * D;
+    k += ((size_t)bh * a.Sk + kbeg) * D;
+    v += ((size_t)bh * a.Sk + kbeg) * D;
+    o += blockIdx.y * a.o_split + (size_t)bh * S * D;
+    lse += blockIdx.y * a.l_split + (size_t)bh * S;
     const int q0 = qt * C::BQ;
     const int qw0 = q0 + wave * NQB * 32;
 
@@ -108,14 +129,17 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
     }
 
     const int qend = min(q0 + C::BQ, S);
-    int nkt = (S + BK - 1) / BK;
-    if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
+    int nkt = (Sk + BK - 1) / BK;
+    if (causal) {
+        const int last = qend - 1 + off;  // last key any query of the tile may see
+        nkt = last < 0 ? 0 : min(nkt, last / BK + 1);
+    }
 
     typename C::DMA dma;
     const int half = wave / (C::NW / 2), hw = wave % (C::NW / 2);
     dma.init(lane, hw);
     // this wave's share of key/value tile j: K (first half of the waves) or V
-    auto issue = [&](T *nK, T *nV, int j) { dma.issue(half ? nV : nK, half ? v : k, j * BK, S, hw); };
+    auto issue = [&](T *nK, T *nV, int j) { dma.issue(half ? nV : nK, half ? v : k, j * BK, Sk, hw); };
     issue(sK0, sV0, 0);
     issue(sK1, sV1, 1);
 
@@ -130,17 +154,17 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
         // before the next LDS read.
         // (parts: one before each S^T block and each O^T block)
         constexpr int NP = 2 * C::NKB;
-        const auto rs = C::DMA::range(half ? v : k, (j + 2) * BK, S);
+        const auto rs = C::DMA::range(half ? v : k, (j + 2) * BK, Sk);
         T *const nT = half ? nV : nK;
-        const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
+        const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1 + off);
         if (!active) {
-            dma.issue(nT, half ? v : k, (j + 2) * BK, S, hw);
+            dma.issue(nT, half ? v : k, (j + 2) * BK, Sk, hw);
         } else {
             // S^T block (kb, qb): rows = keys j0 + 32*kb + ridx(r, h), col = query.
             f32x16 s[NQB][C::NKB];
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
-                dma.template issue_part<NP>(kb, nT, rs, hw);
+                dma.issue_part(kb, NP, nT, rs, hw);
                 // K fragments are read in groups of KG (each feeds NQB
                 // products; an odd count ends with a single one): with two
                 // query blocks per wave the registers would not hold them all
@@ -162,7 +186,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
                 if constexpr (C::NSD % KG != 0)
                     group(std::integral_constant<int, C::NSD % KG>{}, C::NSD / KG * KG);
             }
-            const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
+            const bool need_mask = (causal && j0 + BK - 1 > qw0 + off) || (j0 + BK > Sk);
             if (need_mask) {
                 // (the empty volatile asm keeps this block a real branch: only
                 // tiles crossing the diagonal or the sequence end pay for masking)
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     const int qi = qw0 + qb * 32 + l32;
-                    const int lim = causal ? min(qi + 1, S) : S;
+                    const int lim = causal ? min(qi + 1 + off, Sk) : Sk;
                     const int t = lim - j0 - 2 * h;
 #pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb)
@@ -193,7 +217,9 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
                 const bool grow = mx > mrow[qb] + kRescaleSlack;
                 if (__ballot(grow) != 0) {  // wave-uniform: rare after the first tile
                     const float mnew = grow ? mx : mrow[qb];
-                    const float alpha = fast_exp2(mrow[qb] - mnew);
+                    // (a row that has seen no key yet keeps -inf: its alpha is 1,
+                    // not exp2(-inf - -inf))
+                    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mrow[qb] - mnew);
                     lrow[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
@@ -215,7 +241,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
             // O^T += V^T P^T
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
-                dma.template issue_part<NP>(C::NKB + kb, nT, rs, hw);
+                dma.issue_part(C::NKB + kb, NP, nT, rs, hw);
                 frag pf[NQB][C::NI];
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) to_bfrag<T>(pf[qb], s[qb][kb]);
@@ -245,67 +271,112 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(const T *__restrict__ q, con
         const int qi = qw0 + qb * 32 + l32;
         const float lt = wave_xor32_sum(lrow[qb]);
         if (qi < S) {
-            const float inv = 1.f / lt;
+            // a row that allows no key of this launch (shifted or split keys
+            // only) has the empty result O = 0, L = -inf
+            const bool empty = !(lt > 0.f);
+            const float inv = empty ? 0.f : 1.f / lt;
 #pragma unroll
             for (int db = 0; db < C::ND; ++db)
 #pragma unroll
                 for (int hr = 0; hr < 2; ++hr) {
                     const int d0 = db * 32 + 16 * hr + 8 * h;
-                    if (d0 < D) store8<T>(o + (size_t)qi * D + d0, acc[qb][db], 8 * hr, inv);
+                    if (d0 < D) store8<OutT>(o + (size_t)qi * D + d0, acc[qb][db], 8 * hr, inv);
                 }
-            if (h == 0) lse[qi] = (mrow[qb] + log2f(lt)) * kLn2;
+            if (h == 0) lse[qi] = empty ? -INFINITY : (mrow[qb] + log2f(lt)) * kLn2;
         }
     }
 }
 
-template <typename T, typename C>
-static int run_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int BH, int S,
-                   float scale, int causal, hipStream_t stream) {
-    const int nqt = (S + C::BQ - 1) / C::BQ;
-    const long long grid = (long long)nqt * BH;
-    if (grid > 0x7fffffffLL) return -1;
-    hipLaunchKernelGGL((fwd_kernel<T, C>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, (T *)o, lse, BH, S, scale * kLog2e,
-                       causal, nqt);
+template <typename T, typename C, typename OutT, bool GEN>
+static int run_fwd(const void *q, const void *k, const void *v, OutT *o, float *lse, FwdShape a,
+                   int n_split, hipStream_t stream) {
+    a.nqt = (a.Sq + C::BQ - 1) / C::BQ;
+    const long long grid = (long long)a.nqt * a.BH;
+    if (grid > 0x7fffffffLL || n_split > 65535) return -1;
+    hipLaunchKernelGGL((fwd_kernel<T, C, OutT, GEN>), dim3((unsigned)grid, (unsigned)n_split), dim3(C::NT), 0,
+                       stream, (const T *)q, (const T *)k, (const T *)v, o, lse, a);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+// Key-tile rows: fp32 rows are twice the bytes, so wide fp32 heads take
+// 32-key tiles to fit three stages.
 template <typename T, int D>
-static int fwd_for(const void *q, const void *k, const void *v, void *o, float *lse, int BH, int S,
-                   float scale, int causal, hipStream_t stream) {
-    // fp32 rows are twice the bytes: wide fp32 heads take 32-key tiles to fit three stages
-    constexpr int BK = (sizeof(T) == 4 && D > 80) ? 32 : 64;
+constexpr int fwd_bk() { return (sizeof(T) == 4 && D > 80) ? 32 : 64; }
+
+template <typename T, int D, typename OutT, bool GEN>
+static int fwd_for(const void *q, const void *k, const void *v, OutT *o, float *lse, const FwdShape &a,
+                   int n_split, hipStream_t stream) {
+    constexpr int BK = fwd_bk<T, D>();
     // bf16 D=128: 64 queries per wave over 32-key tiles halves the K/V reads
     // per FLOP, but makes the query tiles twice as long; keep it for problems
     // with at least four such tiles per CU (short causal problems lose more
     // to the uneven tile lengths than they gain).  Measured slower at D=80.
     using C2 = FwdTile<T, D, 2, 32, 8>;
-    if constexpr (sizeof(T) == 2 && D == 128) {
-        const long long tiles2 = (long long)((S + C2::BQ - 1) / C2::BQ) * BH;
-        if (tiles2 >= 4 * kNumCU) return run_fwd<T, C2>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    if constexpr (sizeof(T) == 2 && D == 128 && !GEN) {
+        const long long tiles2 = (long long)((a.Sq + C2::BQ - 1) / C2::BQ) * a.BH;
+        if (tiles2 >= 4 * kNumCU) return run_fwd<T, C2, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
     }
-    return run_fwd<T, FwdTile<T, D, 1, BK, 8>>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    return run_fwd<T, FwdTile<T, D, 1, BK, 8>, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
 }
 
-template <typename T>
-static int fwd_dispatch(int D, const void *q, const void *k, const void *v, void *o, float *lse,
-                        int BH, int S, float scale, int causal, hipStream_t stream) {
+template <typename T, bool GEN, typename OutT>
+static int fwd_dispatch(int D, const void *q, const void *k, const void *v, OutT *o, float *lse,
+                        const FwdShape &a, int n_split, hipStream_t stream) {
     switch (D) {
-    case 16: return fwd_for<T, 16>(q, k, v, o, lse, BH, S, scale, causal, stream);
-    case 32: return fwd_for<T, 32>(q, k, v, o, lse, BH, S, scale, causal, stream);
-    case 64: return fwd_for<T, 64>(q, k, v, o, lse, BH, S, scale, causal, stream);
-    case 80: return fwd_for<T, 80>(q, k, v, o, lse, BH, S, scale, causal, stream);
-    case 96: return fwd_for<T, 96>(q, k, v, o, lse, BH, S, scale, causal, stream);
-    case 128: return fwd_for<T, 128>(q, k, v, o, lse, BH, S, scale, causal, stream);
+    case 16: return fwd_for<T, 16, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    case 32: return fwd_for<T, 32, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    case 64: return fwd_for<T, 64, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    case 80: return fwd_for<T, 80, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    case 96: return fwd_for<T, 96, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    case 128: return fwd_for<T, 128, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
     default: return -2;
     }
 }
 
 int launch_fwd(int dtype, const void *q, const void *k, const void *v, void *o, float *lse, int BH,
                int S, int D, float scale, int causal, hipStream_t stream) {
-    if (dtype == 1) return fwd_dispatch<bf16>(D, q, k, v, o, lse, BH, S, scale, causal, stream);
-    if (dtype == 0) return fwd_dispatch<float>(D, q, k, v, o, lse, BH, S, scale, causal, stream);
+    FwdShape a{BH, S, S, 0, S, causal, 0, scale * kLog2e, 0, 0};
+    if (dtype == 1) return fwd_dispatch<bf16, false>(D, q, k, v, (bf16 *)o, lse, a, 1, stream);
+    if (dtype == 0) return fwd_dispatch<float, false>(D, q, k, v, (float *)o, lse, a, 1, stream);
     return -2;
 }
+
+int launch_fwd_partial(int dtype, const void *q, const void *k, const void *v, float *o_parts,
+                       float *lse_parts, int BH, int Sq, int Sk, int D, float scale, int causal,
+                       int q_offset, int n_split, int chunk, hipStream_t stream) {
+    FwdShape a{BH, Sq, Sk, q_offset, chunk, causal, 0, scale * kLog2e, (long long)BH * Sq * D,
+               (long long)BH * Sq};
+    if (dtype == 1) return fwd_dispatch<bf16, true>(D, q, k, v, o_parts, lse_parts, a, n_split, stream);
+    if (dtype == 0) return fwd_dispatch<float, true>(D, q, k, v, o_parts, lse_parts, a, n_split, stream);
+    return -2;
+}
+
+// Every kernel the dispatch above can launch, instantiated explicitly: the
+// host compilation pass has been seen to drop the launch stubs of some
+// implicitly instantiated kernel templates (an undefined symbol at load
+// time), so the list is spelled out.
+#define COMMA ,
+#define FA_FWD_KERNEL(T, C, OUT, GEN)                                                                         \
+    template __global__ void fwd_kernel<T, C, OUT, GEN>(const T *, const T *, const T *, OUT *, float *,     \
+                                                        FwdShape);
+#define FA_FWD_HEAD(T, D)                                                                        \
+    FA_FWD_KERNEL(T, FwdTile<T COMMA D COMMA 1 COMMA fwd_bk<T COMMA D>() COMMA 8>, T, false)    \
+    FA_FWD_KERNEL(T, FwdTile<T COMMA D COMMA 1 COMMA fwd_bk<T COMMA D>() COMMA 8>, float, true)
+FA_FWD_HEAD(bf16, 16)
+FA_FWD_HEAD(bf16, 32)
+FA_FWD_HEAD(bf16, 64)
+FA_FWD_HEAD(bf16, 80)
+FA_FWD_HEAD(bf16, 96)
+FA_FWD_HEAD(bf16, 128)
+FA_FWD_HEAD(float, 16)
+FA_FWD_HEAD(float, 32)
+FA_FWD_HEAD(float, 64)
+FA_FWD_HEAD(float, 80)
+FA_FWD_HEAD(float, 96)
+FA_FWD_HEAD(float, 128)
+FA_FWD_KERNEL(bf16, FwdTile<bf16 COMMA 128 COMMA 2 COMMA 32 COMMA 8>, bf16, false)
+#undef FA_FWD_HEAD
+#undef FA_FWD_KERNEL
+#undef COMMA
 
 }  // namespace fa

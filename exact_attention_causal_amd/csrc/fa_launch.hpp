@@ -20,6 +20,15 @@ inline bool head_dim_supported(int D) {
 int launch_fwd(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
                int BH, int S, int D, float scale, int causal, hipStream_t stream);
 
+// Shifted / split-key forward with fp32 partial outputs; `chunk` keys per split.
+int launch_fwd_partial(int dtype, const void *q, const void *k, const void *v, float *o_parts,
+                       float *lse_parts, int BH, int Sq, int Sk, int D, float scale, int causal,
+                       int q_offset, int n_split, int chunk, hipStream_t stream);
+
+// Merge of n partial results (rows = B*H*S).
+int launch_merge(int dtype, const float *o_parts, const float *lse_parts, int n, void *o, float *lse,
+                 long long rows, int D, hipStream_t stream);
+
 int launch_delta(int dtype, const void *o, const void *dout, float *delta, int BH, int S, int D,
                  hipStream_t stream);
 

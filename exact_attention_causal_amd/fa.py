@@ -1,7 +1,7 @@
 """ctypes binding of the gfx950 attention library (include/fa.h).
 
 The functions named like the C entry points (fa_fwd, fa_bwd_preprocess,
-fa_bwd_workspace_size, fa_bwd, fa_strerror) only marshal arguments: tensors
+fa_bwd_workspace_size, fa_bwd, fa_fwd_partial, fa_merge, fa_strerror) only marshal arguments: tensors
 become device pointers, the stream becomes HIP's stream handle, and the status
 code comes back unchanged.  ``forward`` / ``backward`` / ``attention_fwd_bwd``
 are conveniences that allocate outputs with PyTorch (device memory is the
@@ -61,6 +61,10 @@ def load_library():
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [_vp] * 10 + [ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _i, _vp]
     lib.fa_bwd.restype = _i
+    lib.fa_fwd_partial.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _i, _i, _i, _vp]
+    lib.fa_fwd_partial.restype = _i
+    lib.fa_merge.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+    lib.fa_merge.restype = _i
     lib.fa_strerror.argtypes = [_i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -105,6 +109,18 @@ def fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes, B,
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                  int(workspace_bytes), B, H, S, D, float(scale), int(causal),
                                  int(dtype), _stream(stream))
+
+
+def fa_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Sq, Sk, D, scale, causal, q_offset, n_split,
+                   dtype, stream=None):
+    return load_library().fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o_parts), _ptr(lse_parts),
+                                         B, H, Sq, Sk, D, float(scale), int(causal), int(q_offset),
+                                         int(n_split), int(dtype), _stream(stream))
+
+
+def fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, S, D, dtype, stream=None):
+    return load_library().fa_merge(_ptr(o_parts), _ptr(lse_parts), int(n_parts), _ptr(o), _ptr(lse),
+                                   B, H, S, D, int(dtype), _stream(stream))
 
 
 def fa_strerror(status):
@@ -169,6 +185,47 @@ def backward(q, k, v, o, lse, dout, causal=True, scale=None, delta=None, grads=N
     _check(fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, ws_bytes, B, H, S, D, scale,
                   causal, code, stream), "fa_bwd")
     return dq, dk, dv, delta
+
+
+def split_chunk(Sk, n_split):
+    """Keys per chunk of fa_fwd_partial: 64 * ceil(Sk / (64 * n_split))."""
+    return 64 * ((Sk + 64 * n_split - 1) // (64 * n_split))
+
+
+def forward_partial(q, k, v, causal=True, scale=None, q_offset=0, n_split=1, stream=None):
+    """fp32 (O, L) of q [B,H,Sq,D] over each key chunk of k, v [B,H,Sk,D].
+
+    Returns o_parts [n_split, B, H, Sq, D] and lse_parts [n_split, B, H, Sq]; query i
+    sits q_offset positions after key 0 (see fa_fwd_partial in include/fa.h).
+    """
+    B, H, Sq, D = _shape(q)
+    Sk = k.shape[2]
+    q, k, v = (x.contiguous() for x in (q, k, v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o_parts = torch.empty((n_split, B, H, Sq, D), device=q.device, dtype=torch.float32)
+    lse_parts = torch.empty((n_split, B, H, Sq), device=q.device, dtype=torch.float32)
+    _check(fa_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Sq, Sk, D, scale, causal, q_offset,
+                          n_split, dtype_code(q.dtype), stream), "fa_fwd_partial")
+    return o_parts, lse_parts
+
+
+def merge(o_parts, lse_parts, dtype=torch.bfloat16, stream=None):
+    """Merge [n, B, H, S, D] fp32 partial outputs and [n, B, H, S] L into (O in dtype, L)."""
+    n, B, H, S, D = o_parts.shape
+    if not o_parts.is_cuda:
+        raise ValueError("tensors must be on a GPU (there is no CPU path)")
+    o_parts, lse_parts = o_parts.contiguous(), lse_parts.contiguous()
+    o = torch.empty((B, H, S, D), device=o_parts.device, dtype=dtype)
+    lse = torch.empty((B, H, S), device=o_parts.device, dtype=torch.float32)
+    _check(fa_merge(o_parts, lse_parts, n, o, lse, B, H, S, D, dtype_code(dtype), stream), "fa_merge")
+    return o, lse
+
+
+def forward_split_kv(q, k, v, n_split, causal=True, scale=None, stream=None):
+    """Self-attention forward with the keys split over n_split chunks, then merged."""
+    o_parts, lse_parts = forward_partial(q, k, v, causal, scale, 0, n_split, stream)
+    return merge(o_parts, lse_parts, q.dtype, stream)
 
 
 # ------------------------------------------------------------- autograd ---

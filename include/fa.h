@@ -101,6 +101,47 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout,
            int B, int H, int S, int D, float scale, int causal, fa_dtype dtype,
            hipStream_t stream);
 
+/*
+ * Forward pass over shifted and/or split keys, producing partial results to
+ * merge (the ring-attention page "[Attention]FlashAttention/Ring-Attention/
+ * 混合序列并行的统一原理", sections "online softmax" and "online attention":
+ * attention over a key set can be split along the keys and the parts merged
+ * exactly).
+ *   q          : [B][H][Sq][D] queries; query i sits q_offset positions after
+ *                key 0 of this call (causal: key j is allowed iff j <= i + q_offset).
+ *   k, v       : [B][H][Sk][D] keys and values.
+ *   n_split    : the keys are cut into n_split chunks of
+ *                chunk = 64 * ceil(Sk / (64 * n_split)) rows (the last one
+ *                shorter or empty); chunk s holds keys [s*chunk, min((s+1)*chunk, Sk)).
+ *   o_parts    : [n_split][B][H][Sq][D] fp32 output: for every chunk, the
+ *                attention of each query over that chunk's allowed keys
+ *                (normalised within the chunk).
+ *   lse_parts  : [n_split][B][H][Sq] fp32 output: the chunk's
+ *                L_i = ln sum_{j in chunk, allowed} exp(scale * q_i . k_j).
+ *   A row that allows no key of a chunk gets O = 0 and L = -inf there.
+ * With q_offset = 0, Sq = Sk and n_split = 1 this is fa_fwd with fp32 output.
+ * Constraints as fa_fwd, plus Sq, Sk >= 1, 1 <= n_split <= 65535 and
+ * n_split*B*H*Sq*D within 63 bits.
+ */
+int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, float *lse_parts,
+                   int B, int H, int Sq, int Sk, int D, float scale, int causal, int q_offset,
+                   int n_split, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Merge n_parts results over disjoint key sets of the same queries (the same
+ * page, section "online attention": each part's output is rescaled by its
+ * share of the common softmax denominator).  With M = max_r L_r:
+ *   w_r = exp(L_r - M),  O = sum_r w_r O_r / sum_r w_r,  L = M + ln sum_r w_r;
+ * a row empty in every part (all L_r = -inf) gives O = 0, L = -inf.
+ *   o_parts   : [n_parts][B][H][S][D] fp32     lse_parts : [n_parts][B][H][S] fp32
+ *   o         : [B][H][S][D] output in `dtype` lse       : [B][H][S] fp32 output
+ * Parts are combined in a fixed order, so results are reproducible.
+ * Constraints: n_parts >= 1 (and n_parts*B*H*S*D within 63 bits); D and
+ * dtype as fa_fwd.
+ */
+int fa_merge(const float *o_parts, const float *lse_parts, int n_parts, void *o, float *lse,
+             int B, int H, int S, int D, fa_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char *fa_strerror(int status);
 

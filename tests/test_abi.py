@@ -35,7 +35,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_preprocess", "fa_bwd_workspace_size",
-                                     "fa_fwd", "fa_strerror"]
+                                     "fa_fwd", "fa_fwd_partial", "fa_merge", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -109,6 +109,49 @@ def test_preprocess_rejects(lib, bad, code):
 ])
 def test_bwd_rejects(lib, bad, code):
     assert _bwd(**bad) == code
+
+
+def _part(**kw):
+    a = dict(q=P, k=P, v=P, o_parts=P, lse_parts=P, B=1, H=2, Sq=100, Sk=300, D=64, scale=0.125,
+             causal=1, q_offset=200, n_split=3, dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_partial(**a)
+
+
+def _merge(**kw):
+    a = dict(o_parts=P, lse_parts=P, n_parts=3, o=P, lse=P, B=1, H=2, S=100, D=64,
+             dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_merge(**a)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), fa.FA_EINVAL), (dict(lse_parts=None), fa.FA_EINVAL), (dict(Sq=0), fa.FA_EINVAL),
+    (dict(Sk=-1), fa.FA_EINVAL), (dict(n_split=0), fa.FA_EINVAL), (dict(n_split=70000), fa.FA_EINVAL),
+    (dict(causal=3), fa.FA_EINVAL), (dict(scale=0.0), fa.FA_EINVAL), (dict(Sk=(1 << 30) + 1), fa.FA_EINVAL),
+    (dict(B=1 << 16, H=1 << 10, Sq=1 << 20, D=128, n_split=1000), fa.FA_EINVAL),
+    (dict(D=40), fa.FA_EUNSUPPORTED), (dict(dtype=5), fa.FA_EUNSUPPORTED),
+    (dict(o_parts=MIS), fa.FA_EALIGN), (dict(k=MIS), fa.FA_EALIGN),
+])
+def test_fwd_partial_rejects(lib, bad, code):
+    assert _part(**bad) == code
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(o=None), fa.FA_EINVAL), (dict(lse_parts=None), fa.FA_EINVAL), (dict(n_parts=0), fa.FA_EINVAL),
+    (dict(S=0), fa.FA_EINVAL), (dict(B=1 << 16, H=1 << 10, S=1 << 20, D=128, n_parts=1000), fa.FA_EINVAL),
+    (dict(D=24), fa.FA_EUNSUPPORTED), (dict(dtype=9), fa.FA_EUNSUPPORTED),
+    (dict(lse=MIS), fa.FA_EALIGN), (dict(o_parts=P + 8), fa.FA_EALIGN),
+])
+def test_merge_rejects(lib, bad, code):
+    assert _merge(**bad) == code
+
+
+def test_split_chunk_rule():
+    # 64-key multiples covering Sk in n_split chunks (the last one may be short or empty)
+    for Sk, n in ((300, 3), (64, 1), (65, 2), (1, 4), (65536, 7)):
+        c = fa.split_chunk(Sk, n)
+        assert c % 64 == 0 and c * n >= Sk and c * (n - 1) < Sk + 64 * n
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -237,6 +237,103 @@ def test_autograd_function_single_head_layout():
     assert rel(q3.grad.double().cpu().numpy(), r["dq"][:, 0]) <= TOL["bf16"]["grad"]
 
 
+# ------------------------------------- shifted / split keys and the merge ---
+
+def _check_partial(g_o, g_l, r_o, r_l, dtype, label):
+    """Compare fp32 partial (O, L) with the oracle; empty rows must be exactly (0, -inf)."""
+    empty = np.isneginf(r_l)
+    assert np.array_equal(np.isneginf(g_l), empty), label
+    assert np.all(g_o[empty] == 0.0), label
+    if (~empty).any():
+        eo = rel(g_o[~empty], r_o[~empty])
+        el = absdiff(g_l[~empty], r_l[~empty])
+        print(f"[parity] {label} errors o={eo:.3g} lse={el:.3g}", flush=True)
+        assert eo <= TOL[dtype]["o"], (label, eo)
+        assert el <= TOL[dtype]["lse"], (label, el)
+
+
+@pytest.mark.parametrize("Sq,Sk,off,causal", [
+    (100, 300, 200, 1),    # queries after most keys (one shard against an earlier one)
+    (300, 100, -50, 1),    # early queries see no key
+    (77, 77, 0, 1),        # plain causal self-attention
+    (200, 130, 1000, 1),   # every key allowed
+    (64, 200, -64, 1),     # no query sees any key
+    (90, 130, 0, 0),       # no mask
+])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 80)])
+def test_fwd_partial_shifted(Sq, Sk, off, causal, dtype, D):
+    dev = torch.device("cuda:0")
+    q, _, _, _ = make_inputs(2, 2, Sq, D, dtype, seed=600 + Sq)
+    _, k, v, _ = make_inputs(2, 2, Sk, D, dtype, seed=700 + Sk)
+    op, lp = fa.forward_partial(q.to(dev), k.to(dev), v.to(dev), causal=bool(causal), q_offset=off)
+    torch.cuda.synchronize()
+    r_o, r_l = oracle.forward_offset(*(x.double().numpy() for x in (q, k, v)), q_offset=off,
+                                     causal=bool(causal))
+    _check_partial(op[0].double().cpu().numpy(), lp[0].double().cpu().numpy(), r_o, r_l, dtype,
+                   f"partial Sq={Sq} Sk={Sk} off={off} causal={causal} D={D}")
+
+
+@pytest.mark.parametrize("n_split", [2, 3, 7])
+def test_fwd_partial_split_chunks(n_split):
+    # every chunk's (O, L) is attention over that chunk's keys at their positions
+    dev = torch.device("cuda:0")
+    Sq, Sk, off, D = 150, 333, 120, 64
+    q, _, _, _ = make_inputs(1, 3, Sq, D, "bf16", seed=800)
+    _, k, v, _ = make_inputs(1, 3, Sk, D, "bf16", seed=801)
+    op, lp = fa.forward_partial(q.to(dev), k.to(dev), v.to(dev), causal=True, q_offset=off,
+                                n_split=n_split)
+    torch.cuda.synchronize()
+    c = fa.split_chunk(Sk, n_split)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    for s_ in range(n_split):
+        a, b = min(s_ * c, Sk), min((s_ + 1) * c, Sk)
+        if a == b:   # a chunk past the keys is empty for every row
+            assert torch.all(op[s_] == 0) and torch.all(torch.isneginf(lp[s_]))
+            continue
+        r_o, r_l = oracle.forward_offset(qn, kn[:, :, a:b], vn[:, :, a:b], q_offset=off - a,
+                                         causal=True)
+        _check_partial(op[s_].double().cpu().numpy(), lp[s_].double().cpu().numpy(), r_o, r_l,
+                       "bf16", f"split {s_}/{n_split}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_merge_matches_oracle(dtype):
+    dev = torch.device("cuda:0")
+    g = torch.Generator("cpu").manual_seed(900)
+    n, B, H, S, D = 4, 2, 3, 50, 80
+    o_parts = torch.randn(n, B, H, S, D, generator=g)
+    lse_parts = torch.randn(n, B, H, S, generator=g) * 3.0
+    lse_parts[1, 0, 0, :10] = float("-inf")            # a part empty on some rows
+    o_parts[1, 0, 0, :10] = 0.0
+    lse_parts[:, 1, 2, 7] = float("-inf")              # a row empty in every part
+    o_parts[:, 1, 2, 7] = 0.0
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o, lse = fa.merge(o_parts.to(dev), lse_parts.to(dev), tdt)
+    torch.cuda.synchronize()
+    r_o, r_l = oracle.merge(o_parts.double().numpy(), lse_parts.double().numpy())
+    go, gl = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert go[1, 2, 7].tolist() == [0.0] * D and np.isneginf(gl[1, 2, 7])
+    fin = ~np.isneginf(r_l)
+    assert np.array_equal(np.isneginf(gl), ~fin)
+    # fp32 merge arithmetic: 1e-5 relative on an fp32 output, bf16 rounding otherwise
+    assert rel(go, r_o) <= (1e-5 if dtype == "f32" else 8e-3)
+    assert absdiff(gl[fin], r_l[fin]) <= 1e-5
+
+
+@pytest.mark.parametrize("n_split,S,D", [(4, 700, 64), (9, 2000, 128), (2, 100, 80)])
+def test_split_kv_forward_end_to_end(n_split, S, D):
+    dev = torch.device("cuda:0")
+    q, k, v, _ = make_inputs(2, 3, S, D, "bf16", seed=1000 + S)
+    o, lse = fa.forward_split_kv(q.to(dev), k.to(dev), v.to(dev), n_split)
+    o1, l1 = fa.forward(q.to(dev), k.to(dev), v.to(dev))
+    torch.cuda.synchronize()
+    r_o, r_l = oracle.forward(*(x.double().numpy() for x in (q, k, v)), causal=True)
+    assert rel(o.double().cpu().numpy(), r_o) <= TOL["bf16"]["o"]
+    assert absdiff(lse.double().cpu().numpy(), r_l) <= TOL["bf16"]["lse"]
+    # the split path and the one-pass forward agree to bf16 rounding of O
+    assert rel(o.double().cpu().numpy(), o1.double().cpu().numpy()) <= 1e-2
+
+
 def test_custom_scale_and_peaky_scores():
     q, k, v, do = make_inputs(1, 2, 257, 64, "bf16", seed=7, qk_mult=3.0)
     check_full(q, k, v, do, "bf16", causal=True, scale=0.3, label="scale=0.3 peaky")
