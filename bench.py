@@ -111,8 +111,9 @@ def sweep(dev):
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     rows = []
-    print("| dtype | causal | D | S | fwd ms | fwd+bwd ms | fwd TFLOP/s | fwd+bwd TFLOP/s |")
-    print("|---|---|---|---|---|---|---|---|")
+    print("| dtype | causal | D | S | fwd ms | fwd+bwd ms | fwd TFLOP/s | fwd+bwd TFLOP/s | "
+          "split-KV fwd ms (chunks) |")
+    print("|---|---|---|---|---|---|---|---|---|")
     for dtype in ("bf16", "f32"):
         code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
         for causal in (1, 0):
@@ -151,14 +152,28 @@ def sweep(dev):
                         torch.cuda.synchronize()
                         return statistics.median(x.elapsed_time(y) for x, y in ts)
 
+                    # split-KV forward: keys cut into chunks so that about eight
+                    # workgroups per CU exist, then merged (fa_fwd_partial + fa_merge)
+                    n_split = max(1, min(64, (8 * 256) // max(1, (S + 255) // 256), S // 256))
+                    op = torch.empty((n_split, 1, 1, S, D), device=dev, dtype=torch.float32)
+                    lp = torch.empty((n_split, 1, 1, S), device=dev, dtype=torch.float32)
+
+                    def fwd_split():
+                        rc = fa.fa_fwd_partial(q, k, v, op, lp, 1, 1, S, S, D, scale, causal, 0,
+                                               n_split, code, sh)
+                        assert rc == 0, fa.fa_strerror(rc)
+                        rc = fa.fa_merge(op, lp, n_split, o, lse, 1, 1, S, D, code, sh)
+                        assert rc == 0, fa.fa_strerror(rc)
+
                     n = 10 if S >= 16384 else 30
-                    t_f, t_s = timed(fwd, n), timed(step, n)
+                    t_f, t_s, t_sp = timed(fwd, n), timed(step, n), timed(fwd_split, n)
                     pairs = S * (S + 1) // 2 if causal else S * S
                     tf_f = 4 * D * pairs / (t_f * 1e-3) / 1e12
                     tf_s = 14 * D * pairs / (t_s * 1e-3) / 1e12
-                    rows.append(dict(dtype=dtype, causal=causal, D=D, S=S, fwd_ms=t_f, step_ms=t_s))
+                    rows.append(dict(dtype=dtype, causal=causal, D=D, S=S, fwd_ms=t_f, step_ms=t_s,
+                                     split_ms=t_sp, n_split=n_split))
                     print(f"| {dtype} | {causal} | {D} | {S} | {t_f:.4f} | {t_s:.4f} | {tf_f:.1f} | "
-                          f"{tf_s:.1f} |", flush=True)
+                          f"{tf_s:.1f} | {t_sp:.4f} ({n_split}) |", flush=True)
     return rows
 
 
