@@ -31,9 +31,14 @@ CFLAGS = [
 ]
 
 
+# Per-file scheduler choice: the backward kernels measured ~0.5 % faster when
+# the pre-RA scheduler groups memory operations (no effect on results).
+EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
