@@ -38,7 +38,7 @@ DEFAULT_WORKLOAD = "bf16_b1h16_s65536_d128"
 # rocprofv3 --pmc passes (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a
 # plain 1 GiB copy calibrates; see profiles/), keyed by a hash of the forward
 # kernel's sources: once those change, the figure is stale and reported as null.
-FWD_TRAFFIC = {"sources_sha1": "d2ee6b8d0f1c56cf259d0454306b08d2797f8f76", "bytes": 8331415200}
+FWD_TRAFFIC = {"sources_sha1": "ecab222904cb07db8101f826db3905bf9c4191c9", "bytes": 8263241728}
 FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp")
 
 
@@ -112,8 +112,8 @@ def sweep(dev):
     sh = stream.cuda_stream
     rows = []
     print("| dtype | causal | D | S | fwd ms | fwd+bwd ms | fwd TFLOP/s | fwd+bwd TFLOP/s | "
-          "split-KV fwd ms (chunks) |")
-    print("|---|---|---|---|---|---|---|---|---|")
+          "split-KV fwd ms (chunks) | step peak MiB | one S×S fp32 matrix MiB |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
     for dtype in ("bf16", "f32"):
         code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
         for causal in (1, 0):
@@ -167,13 +167,26 @@ def sweep(dev):
 
                     n = 10 if S >= 16384 else 30
                     t_f, t_s, t_sp = timed(fwd, n), timed(step, n), timed(fwd_split, n)
+                    # memory of one fwd+bwd step over the inputs already held: the
+                    # outputs, L and D (no S x S matrix exists at any point)
+                    del op, lp
+                    torch.cuda.synchronize()
+                    base = torch.cuda.memory_allocated()
+                    torch.cuda.reset_peak_memory_stats()
+                    step()
+                    torch.cuda.synchronize()
+                    peak = (torch.cuda.max_memory_allocated() - base) / 2**20
+                    # (this step's buffers were allocated before `base`; report all of them)
+                    peak += sum(t.numel() * t.element_size()
+                                for t in (o, lse, delta, dq, dk, dv)) / 2**20
+                    sxs = S * S * 4 / 2**20
                     pairs = S * (S + 1) // 2 if causal else S * S
                     tf_f = 4 * D * pairs / (t_f * 1e-3) / 1e12
                     tf_s = 14 * D * pairs / (t_s * 1e-3) / 1e12
                     rows.append(dict(dtype=dtype, causal=causal, D=D, S=S, fwd_ms=t_f, step_ms=t_s,
-                                     split_ms=t_sp, n_split=n_split))
+                                     split_ms=t_sp, n_split=n_split, peak_mib=peak))
                     print(f"| {dtype} | {causal} | {D} | {S} | {t_f:.4f} | {t_s:.4f} | {tf_f:.1f} | "
-                          f"{tf_s:.1f} | {t_sp:.4f} ({n_split}) |", flush=True)
+                          f"{tf_s:.1f} | {t_sp:.4f} ({n_split}) | {peak:.2f} | {sxs:.1f} |", flush=True)
     return rows
 
 
