@@ -194,7 +194,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the heads shard across GPUs with no communication, see DESIGN.md)",
+              "(heads shard across GPUs with no communication, so one GPU is measured)",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
