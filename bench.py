@@ -67,6 +67,10 @@ def parse():
                     help="only run the --hold-entry entry point back to back for SECONDS "
                          "(for sampling clocks and board power alongside) and exit")
     ap.add_argument("--hold-entry", default="fwd", choices=("fwd", "bwd"))
+    ap.add_argument("--split-kv", type=int, default=0, metavar="N",
+                    help="only time the split-KV forward of the workload (fa_fwd_partial over N key "
+                         "chunks, then fa_merge) and print its own JSON line: the partial forward "
+                         "against the matrix-core peak, the merge against HBM bandwidth")
     ap.add_argument("--sweep", action="store_true",
                     help="only time the benchmark sweep (B=1, H=1, S = 128 .. 65536 in powers of "
                          "two, D in 16/32/64/128, bf16 and fp32, causal and not), print a "
@@ -97,6 +101,78 @@ def cpu_baseline(w, q, k, v, do, tokens):
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def split_kv(dev, w, n_split, steps, warmup, with_cpu):
+    """Split-KV forward of one workload: fa_fwd_partial over n_split key chunks + fa_merge.
+
+    The partial forward does the same 4*D*pairs FLOPs as fa_fwd (rated against the
+    matrix-core peak); the merge is bound by HBM: it reads n_split fp32 partial
+    outputs and logsumexps and writes O and L (rated against 8 TB/s).
+    """
+    fa.load_library()
+    code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+    B, H, S, D = w.shape
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    q, k, v, _ = workload_inputs(w)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    op = torch.empty((n_split, B, H, S, D), device=dev, dtype=torch.float32)
+    lp = torch.empty((n_split, B, H, S), device=dev, dtype=torch.float32)
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, S), device=dev, dtype=torch.float32)
+
+    def part():
+        rc = fa.fa_fwd_partial(qd, kd, vd, op, lp, B, H, S, S, D, w.scale, 1, 0, n_split, code, sh)
+        assert rc == 0, fa.fa_strerror(rc)
+
+    def merge():
+        rc = fa.fa_merge(op, lp, n_split, o, lse, B, H, S, D, code, sh)
+        assert rc == 0, fa.fa_strerror(rc)
+
+    for _ in range(warmup):
+        part(); merge()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream); part(); e[1].record(stream); merge(); e[2].record(stream)
+    torch.cuda.synchronize()
+    t_part = statistics.median(e[0].elapsed_time(e[1]) for e in ev)
+    t_merge = statistics.median(e[1].elapsed_time(e[2]) for e in ev)
+    pairs = w.causal_pairs()
+    tf = 4 * D * pairs / (t_part * 1e-3) / 1e12
+    esize = 2 if w.dtype == "bf16" else 4
+    mbytes = n_split * B * H * S * (D + 1) * 4 + B * H * S * (D * esize + 4)
+    gbs = mbytes / (t_merge * 1e-3) / 1e9
+    peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_F32
+    rec = {"mode": "split_kv_forward", "config": {"workload": w.name, "n_split": n_split},
+           "steps": steps, "warmup": warmup,
+           "ms": {"fwd_partial": round(t_part, 4), "merge": round(t_merge, 4),
+                  "total": round(t_part + t_merge, 4)},
+           "fwd_tflops": round(4 * D * pairs / ((t_part + t_merge) * 1e-3) / 1e12, 2),
+           "roofline_partial": {"kernel": "fwd_kernel (fa_fwd_partial)", "bound": "mfma",
+                                "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                                "frac": round(tf / peak, 4)},
+           "roofline_merge": {"kernel": "merge_kernel (fa_merge)", "bound": "hbm",
+                              "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                              "frac": round(gbs / 8000.0, 4), "algorithmic_bytes": mbytes}}
+    if with_cpu:
+        # the oracle's merge of the same kind of parts on the first heads (a bounded sample)
+        import numpy as np
+        import oracle
+        hs = max(1, min(B * H, (1 << 28) // (n_split * S * D)))
+        opn = op.view(n_split, B * H, S, D)[:, :hs].double().cpu().numpy()
+        lpn = lp.view(n_split, B * H, S)[:, :hs].double().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.merge(opn, lpn)
+        dt = time.perf_counter() - t0
+        nb = n_split * hs * S * (D + 1) * 8 + hs * S * (D + 1) * 8
+        rec["cpu_baseline"] = {"value": round(nb / dt / 1e9, 3), "unit": "GB/s (fp64)",
+                               "cores": int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count(),
+                               "kind": "oracle", "seconds": dt,
+                               "sample": f"fp64 oracle merge of the same {n_split} parts for {hs} of "
+                                         f"{B * H} heads"}
+    print(json.dumps(rec), flush=True)
 
 
 def sweep(dev):
@@ -212,6 +288,10 @@ def main():
         return
     if args.sweep:
         sweep(dev)
+        return
+    if args.split_kv:
+        split_kv(dev, WORKLOADS[args.workload], args.split_kv, args.steps, args.warmup,
+                 not args.no_cpu_baseline)
         return
     w = WORKLOADS[args.workload]
     fa.load_library()

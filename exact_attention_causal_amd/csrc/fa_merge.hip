@@ -35,13 +35,20 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ o_
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (M != -INFINITY) {
-        for (int r = 0; r < n; ++r) {
+        auto part = [&](int r) {
             const float lr = lse_parts[(long long)r * rows + row];
             const float w = fast_exp2((lr - M) * kLog2e);  // 0 for an empty part
             wsum += w;
             const f32x4 x = *reinterpret_cast<const f32x4 *>(o_parts + ((long long)r * rows + row) * D + c4);
             acc += w * x;
+        };
+        // four parts per round keep four 16-byte loads in flight per lane
+        int r = 0;
+        for (; r + 4 <= n; r += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) part(r + u);
         }
+        for (; r < n; ++r) part(r);
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     if constexpr (sizeof(T) == 2) {
