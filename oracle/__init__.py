@@ -39,8 +39,10 @@ def _load():
     lib.oracle_cols.argtypes = [_dp] * 6 + [_lp, _L, _dp, _dp, _L, _L, _D, _I, _I]
     lib.oracle_fwd_offset.argtypes = [_dp, _dp, _dp, _dp, _dp, _L, _L, _L, _L, _D, _I, _L, _I]
     lib.oracle_merge.argtypes = [_dp, _dp, _L, _dp, _dp, _L, _L]
+    lib.oracle_bwd_partial.argtypes = [_dp] * 9 + [_L, _L, _L, _L, _D, _I, _L, _I]
     for f in (lib.oracle_fwd, lib.oracle_bwd, lib.oracle_probs, lib.oracle_head_stats,
-              lib.oracle_rows, lib.oracle_cols, lib.oracle_fwd_offset, lib.oracle_merge):
+              lib.oracle_rows, lib.oracle_cols, lib.oracle_fwd_offset, lib.oracle_merge,
+              lib.oracle_bwd_partial):
         f.restype = None
     _lib = lib
     return lib
@@ -110,6 +112,29 @@ def merge(o_parts, lse_parts):
     lse = np.empty(lp.shape[1:])
     lib.oracle_merge(_ptr(op), _ptr(lp), n, _ptr(o), _ptr(lse), rows, D)
     return o, lse
+
+
+def backward_partial(q, k, v, dout, lse, delta, q_offset=0, scale=None, causal=True, nthreads=0):
+    """dQ, dK, dV contributions of the keys k, v ([..., Sk, D]) for queries q ([..., Sq, D])
+    placed q_offset positions after key 0, given the full attention's L and Delta ([..., Sq])."""
+    lib = _load()
+    qh, qshape = _heads(q)
+    kh, kshape = _heads(k)
+    vh, _ = _heads(v)
+    doh, _ = _heads(dout)
+    BH, Sq, D = qh.shape
+    Sk = kh.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    lse = _f64(lse).reshape(BH, Sq)
+    delta = _f64(delta).reshape(BH, Sq)
+    dq = np.empty_like(qh)
+    dk = np.empty_like(kh)
+    dv = np.empty_like(kh)
+    lib.oracle_bwd_partial(_ptr(qh), _ptr(kh), _ptr(vh), _ptr(doh), _ptr(lse), _ptr(delta),
+                           _ptr(dq), _ptr(dk), _ptr(dv), BH, Sq, Sk, D, float(scale),
+                           int(bool(causal)), int(q_offset), int(nthreads))
+    return dq.reshape(qshape), dk.reshape(kshape), dv.reshape(kshape)
 
 
 def backward(q, k, v, dout, scale=None, causal=True, nthreads=0):

@@ -384,3 +384,62 @@ void oracle_merge(const double *o_parts, const double *lse_parts, long n, double
         lse[i] = M + log(wsum);
     }
 }
+
+
+/*
+ * Gradient contributions of one key set, given the row statistics L and
+ * Delta of the full attention (over every key set).  With P_ij = exp(s_ij -
+ * L_i) (handout Eq. 14, with the full L), the backward equations Eq. 15-19
+ * are sums over keys, so they split exactly over disjoint key sets: this set
+ * contributes dQ_i += scale sum_{j in set} dS_ij K_j and owns dK_j, dV_j of its
+ * keys summed over these queries.  Key j is allowed for query i iff
+ * j <= i + q_offset (causal); a row with L_i = -inf has no probability mass
+ * and contributes nothing.  Outputs are overwritten:
+ * dq [BH][Sq][D], dk/dv [BH][Sk][D].
+ */
+void oracle_bwd_partial(const double *q, const double *k, const double *v, const double *dout,
+                        const double *lse, const double *delta, double *dq, double *dk,
+                        double *dv, long BH, long Sq, long Sk, long D, double scale, int causal,
+                        long q_offset, int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long h = 0; h < BH; ++h) {
+        const double *qh = q + h * Sq * D, *kh = k + h * Sk * D, *vh = v + h * Sk * D;
+        const double *doh = dout + h * Sq * D;
+        double *dqh = dq + h * Sq * D, *dkh = dk + h * Sk * D, *dvh = dv + h * Sk * D;
+        memset(dqh, 0, sizeof(double) * (size_t)(Sq * D));
+        memset(dkh, 0, sizeof(double) * (size_t)(Sk * D));
+        memset(dvh, 0, sizeof(double) * (size_t)(Sk * D));
+        for (long i = 0; i < Sq; ++i) {
+            const double L = lse[h * Sq + i], Dl = delta[h * Sq + i];
+            if (L == -INFINITY)
+                continue;
+            long nk = Sk;
+            if (causal) {
+                nk = i + 1 + q_offset;
+                if (nk < 0)
+                    nk = 0;
+                if (nk > Sk)
+                    nk = Sk;
+            }
+            const double *qi = qh + i * D, *doi = doh + i * D;
+            double *dqi = dqh + i * D;
+            for (long j = 0; j < nk; ++j) {
+                const double pij = exp(scale * dot(qi, kh + j * D, D) - L);   /* Eq. 13-14 */
+                const double dpij = dot(doi, vh + j * D, D);                   /* Eq. 16 */
+                const double ds = pij * (dpij - Dl);                           /* Eq. 17 */
+                const double *kj = kh + j * D;
+                double *dkj = dkh + j * D, *dvj = dvh + j * D;
+                for (long d = 0; d < D; ++d) {
+                    dqi[d] += scale * ds * kj[d];                              /* Eq. 18 */
+                    dkj[d] += scale * ds * qi[d];                              /* Eq. 19 */
+                    dvj[d] += pij * doi[d];                                    /* Eq. 15 */
+                }
+            }
+        }
+    }
+}

@@ -287,6 +287,66 @@ def test_merge_closed_forms():
     np.testing.assert_allclose(lm, ref_l, atol=1e-14)
 
 
+def _torch_shifted_grads(q, k, v, do, q_offset, causal, scale):
+    """fp64 torch autograd of attention with an explicitly built shifted mask."""
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)).requires_grad_(True) for x in (q, k, v))
+    s = (qt @ kt.transpose(-1, -2)) * scale
+    if causal:
+        i = torch.arange(q.shape[-2])[:, None]
+        j = torch.arange(k.shape[-2])[None, :]
+        s = s.masked_fill(j > i + q_offset, float("-inf"))
+    o = torch.softmax(s, -1) @ vt
+    o.backward(torch.from_numpy(np.ascontiguousarray(do)))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_key_set_backward_sums_to_the_full_backward(causal):
+    """Query and key shards at their positions: the per-pair contributions, with the full
+    L and D, add up to the gradients of the whole attention (torch autograd)."""
+    S, D = 19, 4
+    q, k, v, do = (_rand((2, S, D), t) for t in (110, 111, 112, 113))
+    sc = 1 / math.sqrt(D)
+    r = oracle.backward(q, k, v, do, scale=sc, causal=causal)
+    dq_t, dk_t, dv_t = _torch_shifted_grads(q, k, v, do, 0, causal, sc)
+    np.testing.assert_allclose(r["dq"], dq_t, rtol=0, atol=1e-12)
+    qb, kb = [0, 7, S], [0, 5, 12, S]      # query shards and key sets
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for qa, qe in zip(qb[:-1], qb[1:]):
+        for ka, ke in zip(kb[:-1], kb[1:]):
+            gq, gk, gv = oracle.backward_partial(q[:, qa:qe], k[:, ka:ke], v[:, ka:ke],
+                                                 do[:, qa:qe], r["lse"][:, qa:qe],
+                                                 r["delta_o"][:, qa:qe], q_offset=qa - ka,
+                                                 scale=sc, causal=causal)
+            dq[:, qa:qe] += gq
+            dk[:, ka:ke] += gk
+            dv[:, ka:ke] += gv
+    np.testing.assert_allclose(dq, dq_t, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, dk_t, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, dv_t, rtol=0, atol=1e-12)
+
+
+def test_key_set_backward_special_cases():
+    S, D = 9, 3
+    q, k, v, do = (_rand((1, S, D), t) for t in (120, 121, 122, 123))
+    sc = 1 / math.sqrt(D)
+    r = oracle.backward(q, k, v, do, scale=sc, causal=True)
+    # one set holding every key at offset 0 is the whole backward
+    gq, gk, gv = oracle.backward_partial(q, k, v, do, r["lse"], r["delta_o"], 0, sc, True)
+    np.testing.assert_allclose(gq, r["dq"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(gk, r["dk"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(gv, r["dv"], rtol=0, atol=1e-13)
+    # keys that no query may see contribute nothing; rows with L = -inf contribute nothing
+    gq, gk, gv = oracle.backward_partial(q, k, v, do, r["lse"], r["delta_o"], -S, sc, True)
+    assert not gq.any() and not gk.any() and not gv.any()
+    lse = r["lse"].copy()
+    lse[:] = -np.inf
+    gq, gk, gv = oracle.backward_partial(q, k, v, do, lse, r["delta_o"], 0, sc, True)
+    assert not gq.any() and not gk.any() and not gv.any()
+
+
 # ---------------------------------------- library routine (torch fp64 CPU) ---
 
 @pytest.mark.parametrize("S,D,causal,mult", [(33, 16, True, 1.0), (64, 8, True, 3.0),
