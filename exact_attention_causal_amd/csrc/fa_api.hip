@@ -94,7 +94,8 @@ int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, 
     if (int rc = check_scale(scale)) return rc;
     if (int rc = check_shape(B, H, Sq, D, dtype)) return rc;
     if (int rc = check_shape(B, H, Sk, D, dtype)) return rc;
-    if (Sq > (1 << 30) || Sk > (1 << 30)) return FA_EINVAL;  // positions stay within int
+    // positions and their sums with the offset (at most Sq + Sk + a tile) stay within int
+    if (Sq > (1 << 29) || Sk > (1 << 29)) return FA_EINVAL;
     // n_split copies of the output must still be addressable
     const long long per_split = (long long)B * H * Sq * D;
     if (per_split > 0x3fffffffffffffffLL / n_split) return FA_EINVAL;
@@ -119,6 +120,27 @@ int fa_merge(const float *o_parts, const float *lse_parts, int n_parts, void *o,
     if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return FA_EALIGN;
     return map_launch(fa::launch_merge(dtype, o_parts, lse_parts, n_parts, o, lse, (long long)B * H * S, D,
                                        stream));
+}
+
+int fa_bwd_partial(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+                   const float *delta, float *dq_acc, float *dk_acc, float *dv_acc, int accumulate, int B,
+                   int H, int Sq, int Sk, int D, float scale, int causal, int q_offset, fa_dtype dtype,
+                   hipStream_t stream) {
+    if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk_acc || !dv_acc) return FA_EINVAL;
+    if (causal != 0 && causal != 1) return FA_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return FA_EINVAL;
+    if (int rc = check_scale(scale)) return rc;
+    if (int rc = check_shape(B, H, Sq, D, dtype)) return rc;
+    if (int rc = check_shape(B, H, Sk, D, dtype)) return rc;
+    // positions and their sums with the offset (at most Sq + Sk + a tile) stay within int
+    if (Sq > (1 << 29) || Sk > (1 << 29)) return FA_EINVAL;
+    const void *ptrs[] = {q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return FA_EALIGN;
+    // offsets beyond [-Sq, Sk] change nothing (every key allowed / none)
+    const int off = (int)(q_offset < -Sq ? -Sq : (q_offset > Sk ? Sk : q_offset));
+    return map_launch(fa::launch_bwd_partial(dtype, q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc,
+                                             accumulate, B * H, Sq, Sk, D, scale, causal, off, stream));
 }
 
 const char *fa_strerror(int status) {

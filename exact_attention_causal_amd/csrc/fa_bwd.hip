@@ -82,6 +82,43 @@ __global__ __launch_bounds__(256) void delta_kernel(const T *__restrict__ o, con
 // separates them, and each wave's vector work (exponentials, dS) overlaps its
 // partner's matrix products on the shared SIMD.
 
+// Problem shape of one backward launch.  Query i sits `off` positions after
+// key 0, so the causal mask allows key j iff j <= i + off (off = 0 and
+// Sq = Sk for self-attention).  With GEN = false (self-attention) the shift is
+// a compile-time zero and the gradients are written in the input dtype; with
+// GEN = true they are fp32 contributions of this key set, added to the
+// outputs when `accumulate` is set.  L and D are the statistics of the whole
+// attention, so a row with L = -inf allows no key of this set either: every
+// tile holding such a row crosses the causal boundary, and the mask zeroes
+// the row's P (the infinite exponential is selected away, never multiplied).
+struct BwdShape {
+    int BH, Sq, Sk, off, causal, nqt, accumulate;
+    float c, scale;  // c = scale * log2(e)
+};
+
+// 8 consecutive gradient values of one lane, times `mul`, stored or (GEN)
+// added to the fp32 output.
+template <bool GEN, typename OutT>
+__device__ inline void out8(OutT *dst, const f32x16 &acc, int r0, float mul, int accumulate) {
+    if constexpr (GEN) {
+        f32x16 x = acc;
+        if (accumulate) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(dst);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(dst + 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x[r0 + t] = fmaf(x[r0 + t], mul, a[t]);
+                x[r0 + 4 + t] = fmaf(x[r0 + 4 + t], mul, b[t]);
+            }
+            store8<OutT>(dst, x, r0, 1.f);
+        } else {
+            store8<OutT>(dst, x, r0, mul);
+        }
+    } else {
+        store8<OutT>(dst, acc, r0, mul);
+    }
+}
+
 template <typename T, int D_, int BQ2_>
 struct KvTile {
     static constexpr int D = D_, BQ2 = BQ2_;
@@ -103,13 +140,12 @@ struct KvTile {
     static_assert(D % 16 == 0 && BQ2 % 32 == 0 && BQ2 <= kWave, "tile shape");
 };
 
-template <typename T, typename C>
+template <typename T, typename C, typename OutT, bool GEN>
 __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                      const T *__restrict__ v, const T *__restrict__ dout,
                                                      const float *__restrict__ lse,
-                                                     const float *__restrict__ delta, T *__restrict__ dk,
-                                                     T *__restrict__ dv, int BH, int S, float c,
-                                                     float scale, int causal) {
+                                                     const float *__restrict__ delta, OutT *__restrict__ dk,
+                                                     OutT *__restrict__ dv, BwdShape a) {
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, BQ2 = C::BQ2;
@@ -127,16 +163,19 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     const int role = wave / C::NPAIR;   // 0: P / dV wave, 1: dS / dK wave
     const int pair = wave % C::NPAIR;
     const int h = lane >> 5, l32 = lane & 31;
+    const int BH = a.BH, S = a.Sq, causal = a.causal;
+    const int Sk = GEN ? a.Sk : S;    // keys of the head (queries: S)
+    const int off = GEN ? a.off : 0;  // query i sits off positions after key 0
+    const float c = a.c;
     const int bid = blockIdx.x;
     const int kt = bid / BH;  // ascending: the tiles with the most query tiles go first
     const int bh = bid % BH;
-    const size_t hoff = (size_t)bh * S * D;
-    q += hoff;
-    k += hoff;
-    v += hoff;
-    dout += hoff;
-    dk += hoff;
-    dv += hoff;
+    q += (size_t)bh * S * D;
+    dout += (size_t)bh * S * D;
+    k += (size_t)bh * Sk * D;
+    v += (size_t)bh * Sk * D;
+    dk += (size_t)bh * Sk * D;
+    dv += (size_t)bh * Sk * D;
     lse += (size_t)bh * S;
     delta += (size_t)bh * S;
     const int k0 = kt * C::BKV;
@@ -146,7 +185,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     // B operand of this wave's first product: K^T (P wave) or V^T (dS wave);
     // lane owns key `key`, d-run of half h.
     frag bf[C::NSD];
-    if (key < S)
+    if (key < Sk)
         load_run<T, C::NSD>(bf, (role ? v : k) + (size_t)key * D + h * (D / 2));
     else
         zero_run<T, C::NSD>(bf);
@@ -162,7 +201,10 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     for (int db = 0; db < C::ND; ++db) acc[db] = f32x16{};
 
     const int nq2 = (S + BQ2 - 1) / BQ2;
-    const int i0 = causal ? k0 / BQ2 : 0;
+    // first query tile that sees key k0 (none at all: i0 = nq2, one empty step)
+    const int i0 = !causal ? 0
+                   : GEN   ? __builtin_amdgcn_readfirstlane(min(max(0, k0 - off) / BQ2, nq2))
+                           : k0 / BQ2;
     const int ntile = nq2 - i0;
 
     typename C::DMA dma;
@@ -260,13 +302,13 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) acc[db] = M::run(a[i], pp[qb][i], acc[db]);  // Eq. 15
                 }
-            const bool need_mask = (causal && kw0 + 31 > q0) || (q0 + BQ2 > S);
+            const bool need_mask = (causal && kw0 + 31 > q0 + off) || (q0 + BQ2 > S);
             if (need_mask) {
                 asm volatile("");  // a real branch: only diagonal / tail tiles pay for masking
                 // query q0 + 32*qb + ridx(r, h) is kept iff it is at least `lo` and below `hi`
 #pragma unroll
                 for (int qb = 0; qb < C::NQ2; ++qb) {
-                    const int lo = (causal ? key : 0) - q0 - 32 * qb - 2 * h;
+                    const int lo = (causal ? key - off : 0) - q0 - 32 * qb - 2 * h;
                     const int hi = S - q0 - 32 * qb - 2 * h;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -333,15 +375,15 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     }
     wait_vmcnt<0>();
 
-    if (key < S) {
-        T *out = role ? dk : dv;
-        const float mul = role ? -scale : 1.f;
+    if (key < Sk) {
+        OutT *out = role ? dk : dv;
+        const float mul = role ? -a.scale : 1.f;
 #pragma unroll
         for (int db = 0; db < C::ND; ++db)
 #pragma unroll
             for (int hr = 0; hr < 2; ++hr) {
                 const int d0 = db * 32 + 16 * hr + 8 * h;
-                if (d0 < D) store8<T>(out + (size_t)key * D + d0, acc[db], 8 * hr, mul);
+                if (d0 < D) out8<GEN>(out + (size_t)key * D + d0, acc[db], 8 * hr, mul, a.accumulate);
             }
     }
 }
@@ -363,13 +405,12 @@ struct QTile {
     static_assert(D % 16 == 0 && BK % 32 == 0 && NW % 2 == 0, "tile shape");
 };
 
-template <typename T, typename C>
+template <typename T, typename C, typename OutT, bool GEN>
 __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                    const T *__restrict__ v, const T *__restrict__ dout,
                                                    const float *__restrict__ lse,
-                                                   const float *__restrict__ delta, T *__restrict__ dq,
-                                                   int BH, int S, float c, float scale, int causal,
-                                                   int nqt) {
+                                                   const float *__restrict__ delta, OutT *__restrict__ dq,
+                                                   BwdShape a) {
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D, NQB = C::NQB, BK = C::BK;
@@ -380,15 +421,18 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
+    const int BH = a.BH, S = a.Sq, causal = a.causal;
+    const int Sk = GEN ? a.Sk : S;    // keys of the head (queries: S)
+    const int off = GEN ? a.off : 0;  // query i sits off positions after key 0
+    const float c = a.c;
     const int bid = blockIdx.x;
-    const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
+    const int qt = causal ? (a.nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
-    const size_t hoff = (size_t)bh * S * D;
-    q += hoff;
-    k += hoff;
-    v += hoff;
-    dout += hoff;
-    dq += hoff;
+    q += (size_t)bh * S * D;
+    dout += (size_t)bh * S * D;
+    dq += (size_t)bh * S * D;
+    k += (size_t)bh * Sk * D;
+    v += (size_t)bh * Sk * D;
     lse += (size_t)bh * S;
     delta += (size_t)bh * S;
     const int q0 = qt * C::BQ;
@@ -404,6 +448,8 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
             load_run<T, C::NSD>(qf[qb], q + (size_t)qi * D + h * (D / 2));
             load_run<T, C::NSD>(df[qb], dout + (size_t)qi * D + h * (D / 2));
             lq[qb] = lse[qi] * kLog2e;
+            // a row without probability mass (L = -inf) gives P = 0
+            if (GEN && lq[qb] == -INFINITY) lq[qb] = INFINITY;
             dl[qb] = delta[qi];
         } else {
             zero_run<T, C::NSD>(qf[qb]);
@@ -427,13 +473,16 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
         for (int db = 0; db < C::ND; ++db) acc[qb][db] = f32x16{};
 
     const int qend = min(q0 + C::BQ, S);
-    int nkt = (S + BK - 1) / BK;
-    if (causal) nkt = min(nkt, (qend - 1) / BK + 1);
+    int nkt = (Sk + BK - 1) / BK;
+    if (causal) {
+        const int last = qend - 1 + off;  // last key any query of the tile sees
+        nkt = last < 0 ? 0 : min(nkt, last / BK + 1);
+    }
 
     typename C::DMA dma;
     const int half = wave / (C::NW / 2), hw = wave % (C::NW / 2);
     dma.init(lane, hw);
-    auto issue = [&](T *nK, T *nV, int j) { dma.issue(half ? nV : nK, half ? v : k, j * BK, S, hw); };
+    auto issue = [&](T *nK, T *nV, int j) { dma.issue(half ? nV : nK, half ? v : k, j * BK, Sk, hw); };
     issue(sK0, sV0, 0);
     issue(sK1, sV1, 1);
 
@@ -443,13 +492,13 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
         lds_barrier();
         // prefetch of tile j+2, unconditional and spread over the key blocks
         // (see the forward kernel)
-        const auto rs = C::DMA::range(half ? v : k, (j + 2) * BK, S);
+        const auto rs = C::DMA::range(half ? v : k, (j + 2) * BK, Sk);
         T *const nT = half ? nV : nK;
-        const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1);
+        const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1 + off);
         if (!active) {
-            dma.issue(nT, half ? v : k, (j + 2) * BK, S, hw);
+            dma.issue(nT, half ? v : k, (j + 2) * BK, Sk, hw);
         } else {
-            const bool need_mask = (causal && j0 + BK - 1 > qw0) || (j0 + BK > S);
+            const bool need_mask = (causal && j0 + BK - 1 > qw0 + off) || (j0 + BK > Sk);
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -476,7 +525,7 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
                         for (int st = 0; st < C::NSD; ++st) dp = M::run(va[st], df[qb][st], dp);
                     }
                     const int qi = qw0 + qb * 32 + l32;
-                    const int t = (causal ? min(qi + 1, S) : S) - j0 - 32 * kb - 2 * h;
+                    const int t = (causal ? min(qi + 1 + off, Sk) : Sk) - j0 - 32 * kb - 2 * h;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lq[qb]));  // Eq. 14
                     if (need_mask) {
@@ -516,7 +565,7 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
                 for (int hr = 0; hr < 2; ++hr) {
                     const int d0 = db * 32 + 16 * hr + 8 * h;
-                    if (d0 < D) store8<T>(dq + (size_t)qi * D + d0, acc[qb][db], 8 * hr, -scale);
+                    if (d0 < D) out8<GEN>(dq + (size_t)qi * D + d0, acc[qb][db], 8 * hr, -a.scale, a.accumulate);
                 }
         }
     }
@@ -534,24 +583,27 @@ static int delta_for(const void *o, const void *dout, float *delta, int BH, int 
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+// Tile shapes: fp32 rows are twice the bytes, so wider fp32 heads take
+// shorter tiles to fit three stages in LDS.
 template <typename T, int D>
+using KvTileFor = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
+template <typename T, int D>
+using QTileFor = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
+
+template <typename T, int D, typename OutT, bool GEN>
 static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
-                   const float *delta, void *dq, void *dk, void *dv, int BH, int S, float scale,
-                   int causal, hipStream_t stream) {
-    using KC = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
-    using QC = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
-    const float c = scale * kLog2e;
-    const long long g1 = (long long)((S + KC::BKV - 1) / KC::BKV) * BH;
-    const int nqt = (S + QC::BQ - 1) / QC::BQ;
-    const long long g2 = (long long)nqt * BH;
+                   const float *delta, OutT *dq, OutT *dk, OutT *dv, BwdShape a, hipStream_t stream) {
+    using KC = KvTileFor<T, D>;
+    using QC = QTileFor<T, D>;
+    const long long g1 = (long long)((a.Sk + KC::BKV - 1) / KC::BKV) * a.BH;
+    a.nqt = (a.Sq + QC::BQ - 1) / QC::BQ;
+    const long long g2 = (long long)a.nqt * a.BH;
     if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
-    hipLaunchKernelGGL((dkdv_kernel<T, KC>), dim3((unsigned)g1), dim3(KC::NT), 0, stream, (const T *)q,
-                       (const T *)k, (const T *)v, (const T *)dout, lse, delta, (T *)dk, (T *)dv, BH, S,
-                       c, scale, causal);
+    hipLaunchKernelGGL((dkdv_kernel<T, KC, OutT, GEN>), dim3((unsigned)g1), dim3(KC::NT), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dk, dv, a);
     if (hipGetLastError() != hipSuccess) return -5;
-    hipLaunchKernelGGL((dq_kernel<T, QC>), dim3((unsigned)g2), dim3(QC::NT), 0, stream, (const T *)q,
-                       (const T *)k, (const T *)v, (const T *)dout, lse, delta, (T *)dq, BH, S, c,
-                       scale, causal, nqt);
+    hipLaunchKernelGGL((dq_kernel<T, QC, OutT, GEN>), dim3((unsigned)g2), dim3(QC::NT), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dq, a);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
@@ -572,11 +624,11 @@ static int delta_dispatch(int D, const void *o, const void *dout, float *delta, 
     FA_D_SWITCH(D, (delta_for<T, DD>(o, dout, delta, BH, S, stream)))
 }
 
-template <typename T>
+template <typename T, typename OutT, bool GEN>
 static int bwd_dispatch(int D, const void *q, const void *k, const void *v, const void *dout,
-                        const float *lse, const float *delta, void *dq, void *dk, void *dv, int BH,
-                        int S, float scale, int causal, hipStream_t stream) {
-    FA_D_SWITCH(D, (bwd_for<T, DD>(q, k, v, dout, lse, delta, dq, dk, dv, BH, S, scale, causal, stream)))
+                        const float *lse, const float *delta, OutT *dq, OutT *dk, OutT *dv,
+                        const BwdShape &a, hipStream_t stream) {
+    FA_D_SWITCH(D, (bwd_for<T, DD, OutT, GEN>(q, k, v, dout, lse, delta, dq, dk, dv, a, stream)))
 }
 
 int launch_delta(int dtype, const void *o, const void *dout, float *delta, int BH, int S, int D,
@@ -589,11 +641,52 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
 int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
                const float *lse, const float *delta, void *dq, void *dk, void *dv, int BH, int S,
                int D, float scale, int causal, hipStream_t stream) {
+    const BwdShape a{BH, S, S, 0, causal, 0, 0, scale * kLog2e, scale};
     if (dtype == 1)
-        return bwd_dispatch<bf16>(D, q, k, v, dout, lse, delta, dq, dk, dv, BH, S, scale, causal, stream);
+        return bwd_dispatch<bf16, bf16, false>(D, q, k, v, dout, lse, delta, (bf16 *)dq, (bf16 *)dk,
+                                               (bf16 *)dv, a, stream);
     if (dtype == 0)
-        return bwd_dispatch<float>(D, q, k, v, dout, lse, delta, dq, dk, dv, BH, S, scale, causal, stream);
+        return bwd_dispatch<float, float, false>(D, q, k, v, dout, lse, delta, (float *)dq, (float *)dk,
+                                                 (float *)dv, a, stream);
     return -2;
 }
+
+int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, const void *dout,
+                       const float *lse, const float *delta, float *dq, float *dk, float *dv,
+                       int accumulate, int BH, int Sq, int Sk, int D, float scale, int causal,
+                       int q_offset, hipStream_t stream) {
+    const BwdShape a{BH, Sq, Sk, q_offset, causal, 0, accumulate, scale * kLog2e, scale};
+    if (dtype == 1)
+        return bwd_dispatch<bf16, float, true>(D, q, k, v, dout, lse, delta, dq, dk, dv, a, stream);
+    if (dtype == 0)
+        return bwd_dispatch<float, float, true>(D, q, k, v, dout, lse, delta, dq, dk, dv, a, stream);
+    return -2;
+}
+
+// Every kernel the dispatch above can launch, instantiated explicitly (the
+// host compilation pass has been seen to drop the launch stubs of some
+// implicitly instantiated kernel templates).
+#define FA_BWD_KERNELS(T, D, OUT, GEN)                                                                       \
+    template __global__ void dkdv_kernel<T, KvTileFor<T, D>, OUT, GEN>(                                     \
+        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, OUT *, BwdShape);  \
+    template __global__ void dq_kernel<T, QTileFor<T, D>, OUT, GEN>(                                        \
+        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, BwdShape);
+#define FA_BWD_HEAD(T, D)                 \
+    FA_BWD_KERNELS(T, D, T, false)        \
+    FA_BWD_KERNELS(T, D, float, true)
+FA_BWD_HEAD(bf16, 16)
+FA_BWD_HEAD(bf16, 32)
+FA_BWD_HEAD(bf16, 64)
+FA_BWD_HEAD(bf16, 80)
+FA_BWD_HEAD(bf16, 96)
+FA_BWD_HEAD(bf16, 128)
+FA_BWD_HEAD(float, 16)
+FA_BWD_HEAD(float, 32)
+FA_BWD_HEAD(float, 64)
+FA_BWD_HEAD(float, 80)
+FA_BWD_HEAD(float, 96)
+FA_BWD_HEAD(float, 128)
+#undef FA_BWD_HEAD
+#undef FA_BWD_KERNELS
 
 }  // namespace fa

@@ -36,4 +36,10 @@ int launch_bwd(int dtype, const void *q, const void *k, const void *v, const voi
                const float *lse, const float *delta, void *dq, void *dk, void *dv, int BH,
                int S, int D, float scale, int causal, hipStream_t stream);
 
+// Gradient contributions of one key set (fp32, stored or added).
+int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, const void *dout,
+                       const float *lse, const float *delta, float *dq, float *dk, float *dv,
+                       int accumulate, int BH, int Sq, int Sk, int D, float scale, int causal,
+                       int q_offset, hipStream_t stream);
+
 }  // namespace fa

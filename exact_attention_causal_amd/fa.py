@@ -1,7 +1,7 @@
 """ctypes binding of the gfx950 attention library (include/fa.h).
 
 The functions named like the C entry points (fa_fwd, fa_bwd_preprocess,
-fa_bwd_workspace_size, fa_bwd, fa_fwd_partial, fa_merge, fa_strerror) only marshal arguments: tensors
+fa_bwd_workspace_size, fa_bwd, fa_fwd_partial, fa_merge, fa_bwd_partial, fa_strerror) only marshal arguments: tensors
 become device pointers, the stream becomes HIP's stream handle, and the status
 code comes back unchanged.  ``forward`` / ``backward`` / ``attention_fwd_bwd``
 are conveniences that allocate outputs with PyTorch (device memory is the
@@ -65,6 +65,8 @@ def load_library():
     lib.fa_fwd_partial.restype = _i
     lib.fa_merge.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     lib.fa_merge.restype = _i
+    lib.fa_bwd_partial.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _i, _i, _i, _vp]
+    lib.fa_bwd_partial.restype = _i
     lib.fa_strerror.argtypes = [_i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -121,6 +123,14 @@ def fa_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Sq, Sk, D, scale, causal, 
 def fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, S, D, dtype, stream=None):
     return load_library().fa_merge(_ptr(o_parts), _ptr(lse_parts), int(n_parts), _ptr(o), _ptr(lse),
                                    B, H, S, D, int(dtype), _stream(stream))
+
+
+def fa_bwd_partial(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, accumulate, B, H, Sq, Sk, D,
+                   scale, causal, q_offset, dtype, stream=None):
+    return load_library().fa_bwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                         _ptr(delta), _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc),
+                                         int(accumulate), B, H, Sq, Sk, D, float(scale),
+                                         int(causal), int(q_offset), int(dtype), _stream(stream))
 
 
 def fa_strerror(status):
@@ -226,6 +236,34 @@ def forward_split_kv(q, k, v, n_split, causal=True, scale=None, stream=None):
     """Self-attention forward with the keys split over n_split chunks, then merged."""
     o_parts, lse_parts = forward_partial(q, k, v, causal, scale, 0, n_split, stream)
     return merge(o_parts, lse_parts, q.dtype, stream)
+
+
+def backward_partial(q, k, v, dout, lse, delta, causal=True, scale=None, q_offset=0, grads=None,
+                     stream=None):
+    """fp32 gradient contributions of the key set k, v [B,H,Sk,D] for q, dout [B,H,Sq,D].
+
+    lse and delta [B,H,Sq] are the whole attention's L and Delta; query i sits q_offset
+    positions after key 0 (see fa_bwd_partial in include/fa.h).  With grads = (dq, dk, dv)
+    (fp32) the contributions are added to them; otherwise new tensors are returned.
+    """
+    B, H, Sq, D = _shape(q)
+    Sk = k.shape[2]
+    q, k, v, dout = (x.contiguous() for x in (q, k, v, dout))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    accumulate = grads is not None
+    if grads is None:
+        f32 = dict(device=q.device, dtype=torch.float32)
+        grads = (torch.empty((B, H, Sq, D), **f32), torch.empty((B, H, Sk, D), **f32),
+                 torch.empty((B, H, Sk, D), **f32))
+    dq, dk, dv = grads
+    for g in grads:
+        if g.dtype != torch.float32 or not g.is_contiguous():
+            raise ValueError("gradient accumulators must be contiguous fp32 tensors")
+    _check(fa_bwd_partial(q, k, v, dout, lse.contiguous(), delta.contiguous(), dq, dk, dv,
+                          accumulate, B, H, Sq, Sk, D, scale, causal, q_offset,
+                          dtype_code(q.dtype), stream), "fa_bwd_partial")
+    return dq, dk, dv
 
 
 # ------------------------------------------------------------- autograd ---

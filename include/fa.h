@@ -120,7 +120,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout,
  *                L_i = ln sum_{j in chunk, allowed} exp(scale * q_i . k_j).
  *   A row that allows no key of a chunk gets O = 0 and L = -inf there.
  * With q_offset = 0, Sq = Sk and n_split = 1 this is fa_fwd with fp32 output.
- * Constraints as fa_fwd, plus Sq, Sk >= 1, 1 <= n_split <= 65535 and
+ * Constraints as fa_fwd, plus 1 <= Sq, Sk <= 2^29, 1 <= n_split <= 65535 and
  * n_split*B*H*Sq*D within 63 bits.
  */
 int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, float *lse_parts,
@@ -141,6 +141,33 @@ int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, 
  */
 int fa_merge(const float *o_parts, const float *lse_parts, int n_parts, void *o, float *lse,
              int B, int H, int S, int D, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Gradient contributions of one key set, for attention split over keys (the
+ * backward counterpart of fa_fwd_partial).  With the statistics L and Delta of
+ * the whole attention, P_ij = exp(scale * q_i . k_j - L_i) (handout Eq. 14),
+ * and each of dQ, dK, dV (Eq. 15-19) is a sum over keys or over queries, so
+ * disjoint key sets contribute independently: this call adds
+ *   dQ_i += scale * sum_{j in set} dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i,
+ *   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . v_j - Delta_i),
+ * over the allowed pairs (causal: j <= i + q_offset).
+ *   q, dout         : [B][H][Sq][D] queries and output gradient.
+ *   k, v            : [B][H][Sk][D] this key set.
+ *   lse, delta      : [B][H][Sq] fp32 L (from fa_merge of every set, or fa_fwd)
+ *                     and Delta (fa_bwd_preprocess of the final O and dout).
+ *                     A row with L = -inf must allow no key of this set (as
+ *                     it does when L covers every set); it contributes nothing.
+ *   dq_acc          : [B][H][Sq][D] fp32 output.
+ *   dk_acc, dv_acc  : [B][H][Sk][D] fp32 outputs.
+ *   accumulate      : 0 = overwrite the outputs, 1 = add to them.
+ * Outputs are fp32 for either input dtype so that contributions add without
+ * intermediate rounding.  With q_offset = 0, Sq = Sk and accumulate = 0 this
+ * is fa_bwd with fp32 outputs.  Constraints as fa_fwd_partial.
+ */
+int fa_bwd_partial(const void *q, const void *k, const void *v, const void *dout,
+                   const float *lse, const float *delta, float *dq_acc, float *dk_acc,
+                   float *dv_acc, int accumulate, int B, int H, int Sq, int Sk, int D,
+                   float scale, int causal, int q_offset, fa_dtype dtype, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *fa_strerror(int status);

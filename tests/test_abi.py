@@ -34,7 +34,7 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_preprocess", "fa_bwd_workspace_size",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_partial", "fa_bwd_preprocess", "fa_bwd_workspace_size",
                                      "fa_fwd", "fa_fwd_partial", "fa_merge", "fa_strerror"]
 
 
@@ -128,7 +128,7 @@ def _merge(**kw):
 @pytest.mark.parametrize("bad,code", [
     (dict(q=None), fa.FA_EINVAL), (dict(lse_parts=None), fa.FA_EINVAL), (dict(Sq=0), fa.FA_EINVAL),
     (dict(Sk=-1), fa.FA_EINVAL), (dict(n_split=0), fa.FA_EINVAL), (dict(n_split=70000), fa.FA_EINVAL),
-    (dict(causal=3), fa.FA_EINVAL), (dict(scale=0.0), fa.FA_EINVAL), (dict(Sk=(1 << 30) + 1), fa.FA_EINVAL),
+    (dict(causal=3), fa.FA_EINVAL), (dict(scale=0.0), fa.FA_EINVAL), (dict(Sk=(1 << 29) + 1), fa.FA_EINVAL),
     (dict(B=1 << 16, H=1 << 10, Sq=1 << 20, D=128, n_split=1000), fa.FA_EINVAL),
     (dict(D=40), fa.FA_EUNSUPPORTED), (dict(dtype=5), fa.FA_EUNSUPPORTED),
     (dict(o_parts=MIS), fa.FA_EALIGN), (dict(k=MIS), fa.FA_EALIGN),
@@ -145,6 +145,26 @@ def test_fwd_partial_rejects(lib, bad, code):
 ])
 def test_merge_rejects(lib, bad, code):
     assert _merge(**bad) == code
+
+
+def _bpart(**kw):
+    a = dict(q=P, k=P, v=P, dout=P, lse=P, delta=P, dq_acc=P, dk_acc=P, dv_acc=P, accumulate=1,
+             B=1, H=2, Sq=100, Sk=300, D=64, scale=0.125, causal=1, q_offset=200,
+             dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_bwd_partial(**a)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), fa.FA_EINVAL), (dict(delta=None), fa.FA_EINVAL), (dict(dv_acc=None), fa.FA_EINVAL),
+    (dict(Sq=0), fa.FA_EINVAL), (dict(Sk=-3), fa.FA_EINVAL), (dict(accumulate=2), fa.FA_EINVAL),
+    (dict(accumulate=-1), fa.FA_EINVAL), (dict(causal=5), fa.FA_EINVAL), (dict(scale=float("nan")), fa.FA_EINVAL),
+    (dict(Sq=(1 << 29) + 1), fa.FA_EINVAL), (dict(Sk=(1 << 29) + 1), fa.FA_EINVAL), (dict(B=1 << 20, H=1 << 10, Sk=1 << 20, D=128), fa.FA_EINVAL),
+    (dict(D=112), fa.FA_EUNSUPPORTED), (dict(dtype=4), fa.FA_EUNSUPPORTED),
+    (dict(dk_acc=MIS), fa.FA_EALIGN), (dict(lse=P + 4), fa.FA_EALIGN), (dict(dout=MIS), fa.FA_EALIGN),
+])
+def test_bwd_partial_rejects(lib, bad, code):
+    assert _bpart(**bad) == code
 
 
 def test_split_chunk_rule():

@@ -334,6 +334,136 @@ def test_split_kv_forward_end_to_end(n_split, S, D):
     assert rel(o.double().cpu().numpy(), o1.double().cpu().numpy()) <= 1e-2
 
 
+# ------------------------------------------- key-set backward and the ring ---
+
+def _stats_over(q, k, v, do, off, causal):
+    """fp64 L and Delta of attention over k, v (the oracle's), as fp32 inputs for the GPU."""
+    o, lse = oracle.forward_offset(q, k, v, q_offset=off, causal=causal)
+    delta = np.einsum("bhsd,bhsd->bhs", o, do)
+    return lse, delta
+
+
+@pytest.mark.parametrize("Sq,Sk,off,causal", [
+    (100, 300, 200, 1),    # queries after most keys
+    (300, 100, -50, 1),    # early queries see no key (L = -inf rows)
+    (129, 129, 0, 1),      # causal self-attention with a ragged tail
+    (200, 130, 1000, 1),   # every key allowed
+    (64, 200, -64, 1),     # no query sees any key: contributions are exactly zero
+    (90, 230, 0, 0),       # no mask
+    (1, 1, 0, 1),          # one query, one key
+])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 80), ("bf16", 16)])
+def test_bwd_partial_shifted(Sq, Sk, off, causal, dtype, D):
+    dev = torch.device("cuda:0")
+    q, _, _, do = make_inputs(2, 2, Sq, D, dtype, seed=1100 + Sq)
+    _, k, v, _ = make_inputs(2, 2, Sk, D, dtype, seed=1200 + Sk)
+    qn, kn, vn, don = (x.double().numpy() for x in (q, k, v, do))
+    lse, delta = _stats_over(qn, kn, vn, don, off, bool(causal))
+    label = f"bwd partial Sq={Sq} Sk={Sk} off={off} causal={causal} {dtype} D={D}"
+    print(f"[parity] {label}", flush=True)
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).float().to(dev)
+    dq, dk, dv = fa.backward_partial(q.to(dev), k.to(dev), v.to(dev), do.to(dev), f32(lse), f32(delta),
+                                     causal=bool(causal), q_offset=off)
+    torch.cuda.synchronize()
+    r = oracle.backward_partial(qn, kn, vn, don, lse, delta, q_offset=off, causal=bool(causal))
+    no_pair = bool(causal) and off <= -Sq     # the mask allows no (query, key) pair
+    for name, g_, r_ in zip(("dq", "dk", "dv"), (dq, dk, dv), r):
+        g_ = g_.double().cpu().numpy()
+        if no_pair:
+            assert not np.any(g_), (label, name)   # exact zeros where nothing contributes
+            continue
+        if np.max(np.abs(r_)) <= 1e-9:
+            # zero by cancellation (one key: P = 1 and Delta = dP, so dS = 0); the kernel's
+            # fp32 dP - Delta of unit-scale inputs leaves rounding residue only
+            assert np.max(np.abs(g_)) <= 1e-4, (label, name)
+            continue
+        e = rel(g_, r_)
+        print(f"[parity] {label} {name} err={e:.3g}", flush=True)
+        assert e <= TOL[dtype]["grad"], (label, name, e)
+
+
+def test_bwd_partial_accumulates():
+    # accumulate = 1 adds the contributions to what the buffers hold; 0 overwrites
+    dev = torch.device("cuda:0")
+    Sq, Sk, off, D = 150, 333, 120, 64
+    q, _, _, do = make_inputs(1, 3, Sq, D, "bf16", seed=1300)
+    _, k, v, _ = make_inputs(1, 3, Sk, D, "bf16", seed=1301)
+    qn, kn, vn, don = (x.double().numpy() for x in (q, k, v, do))
+    lse, delta = _stats_over(qn, kn, vn, don, off, True)
+    args = [x.to(dev) for x in (q, k, v, do)] + [torch.from_numpy(x).float().to(dev) for x in (lse, delta)]
+    g = torch.Generator("cpu").manual_seed(1302)
+    base = [torch.randn(shape, generator=g) for shape in ((1, 3, Sq, D), (1, 3, Sk, D), (1, 3, Sk, D))]
+    acc = [b.clone().to(dev) for b in base]
+    fa.backward_partial(*args, causal=True, q_offset=off, grads=tuple(acc))
+    fresh = fa.backward_partial(*args, causal=True, q_offset=off)
+    torch.cuda.synchronize()
+    for a_, b_, f_ in zip(acc, base, fresh):
+        # the only rounding between the two is the final fp32 add
+        assert torch.allclose(a_.cpu() - b_, f_.cpu(), rtol=1e-6, atol=1e-5)
+    # a key set no query sees leaves accumulators untouched
+    acc2 = [b.clone().to(dev) for b in base]
+    fa.backward_partial(*args, causal=True, q_offset=-Sq, grads=tuple(acc2))
+    torch.cuda.synchronize()
+    for a_, b_ in zip(acc2, base):
+        assert torch.equal(a_.cpu(), b_)
+
+
+def _shards(S, R):
+    edges = [round(i * S / R) for i in range(R + 1)]
+    return list(zip(edges[:-1], edges[1:]))
+
+
+@pytest.mark.parametrize("S,R,D,skip_masked", [(1000, 3, 64, True), (777, 4, 128, False),
+                                                (4096, 4, 128, True)])
+def test_ring_schedule_matches_full_attention(S, R, D, skip_masked):
+    """Sequence sharded R ways: every query shard meets every key shard (as on a ring of R
+    devices, here in one process), forward parts merged, backward contributions accumulated
+    with the merged L and Delta; the result is the full causal attention and its gradients."""
+    dev = torch.device("cuda:0")
+    B, H = 1, 2
+    q, k, v, do = make_inputs(B, H, S, D, "bf16", seed=1400 + S)
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    sh = _shards(S, R)
+    outs, lses = [], []
+    for qa, qe in sh:
+        parts = [fa.forward_partial(qd[:, :, qa:qe], kd[:, :, ka:ke], vd[:, :, ka:ke], causal=True,
+                                    q_offset=qa - ka)
+                 for ka, ke in sh if not (skip_masked and ka > qe - 1)]
+        o_i, l_i = fa.merge(torch.cat([p[0] for p in parts]), torch.cat([p[1] for p in parts]),
+                            torch.bfloat16)
+        outs.append(o_i)
+        lses.append(l_i)
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq = torch.zeros((B, H, S, D), **f32)
+    dk = torch.zeros((B, H, S, D), **f32)
+    dv = torch.zeros((B, H, S, D), **f32)
+    for i, (qa, qe) in enumerate(sh):
+        delta = torch.empty((B, H, qe - qa), **f32)
+        assert fa.fa_bwd_preprocess(outs[i].contiguous(), dod[:, :, qa:qe].contiguous(), delta, B, H,
+                                    qe - qa, D, fa.FA_BF16) == 0
+        for ka, ke in sh:
+            if skip_masked and ka > qe - 1:
+                continue
+            gq = dq[:, :, qa:qe].contiguous()
+            gk = dk[:, :, ka:ke].contiguous()
+            gv = dv[:, :, ka:ke].contiguous()
+            fa.backward_partial(qd[:, :, qa:qe], kd[:, :, ka:ke], vd[:, :, ka:ke], dod[:, :, qa:qe],
+                                lses[i], delta, causal=True, q_offset=qa - ka, grads=(gq, gk, gv))
+            dq[:, :, qa:qe] = gq
+            dk[:, :, ka:ke] = gk
+            dv[:, :, ka:ke] = gv
+    torch.cuda.synchronize()
+    r = oracle.backward(*(x.double().numpy() for x in (q, k, v, do)), causal=True)
+    g = dict(o=torch.cat(outs, 2), lse=torch.cat(lses, 2), dq=dq, dk=dk, dv=dv)
+    g = {n: t.double().cpu().numpy() for n, t in g.items()}
+    errs = dict(o=rel(g["o"], r["o"]), lse=absdiff(g["lse"], r["lse"]),
+                **{n: rel(g[n], r[n]) for n in ("dq", "dk", "dv")})
+    print(f"[parity] ring S={S} R={R} D={D} errors {errs}", flush=True)
+    assert errs["o"] <= TOL["bf16"]["o"] and errs["lse"] <= TOL["bf16"]["lse"], errs
+    for n in ("dq", "dk", "dv"):
+        assert errs[n] <= TOL["bf16"]["grad"], (n, errs)
+
+
 def test_custom_scale_and_peaky_scores():
     q, k, v, do = make_inputs(1, 2, 257, 64, "bf16", seed=7, qk_mult=3.0)
     check_full(q, k, v, do, "bf16", causal=True, scale=0.3, label="scale=0.3 peaky")
