@@ -135,7 +135,10 @@ struct KvTile {
     // a Q (dO) tile array also carries the tile's L (D) values, 64 per P (dS) wave
     static constexpr int XOFF = DMA::ELEMS;           // element offset of those values
     static constexpr int TILE = DMA::ELEMS + NPAIR * kWave * 4 / (int)sizeof(T);
-    static constexpr int PBLK = 64 * 16;              // P values of one 32x32 block (elements)
+    // P values of one 32x32 block (elements), fragment-major: fragment i of
+    // lane l at i*64*KPL + l*KPL, so the 16-byte accesses of consecutive
+    // lanes are contiguous (a 32-byte lane stride costs LDS bank conflicts)
+    static constexpr int PBLK = 64 * 16;
     static constexpr int PBUF = NPAIR * NQ2 * PBLK;   // P of one query tile (one of two buffers)
     static_assert(D % 16 == 0 && BQ2 % 32 == 0 && BQ2 <= kWave, "tile shape");
 };
@@ -266,8 +269,8 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
         // Tile it+1 is issued whole and unconditionally (see the forward
         // kernel); past the last tile its range is empty.
         issue(nQ, ndO, it + 1);
-        T *pw = sP + (u & 1) * C::PBUF + pair * C::NQ2 * C::PBLK + lane * 16;        // P of tile it
-        const T *pr = sP + ((u + 1) & 1) * C::PBUF + pair * C::NQ2 * C::PBLK + lane * 16;  // P of it-1
+        T *pw = sP + (u & 1) * C::PBUF + pair * C::NQ2 * C::PBLK + lane * C::KPL;        // P of tile it
+        const T *pr = sP + ((u + 1) & 1) * C::PBUF + pair * C::NQ2 * C::PBLK + lane * C::KPL;  // P of it-1
         if (role == 0) {
             // dV^T += dO^T P for tile it-1 (P read back from the buffer this
             // wave wrote in the previous step), and S, P of tile it
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 #pragma unroll
             for (int qb = 0; qb < C::NQ2; ++qb)
 #pragma unroll
-                for (int i = 0; i < C::NI; ++i) pp[qb][i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * C::KPL);
+                for (int i = 0; i < C::NI; ++i) pp[qb][i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * (kWave * C::KPL));
             f32x16 s[C::NQ2];
 #pragma unroll
             for (int qb = 0; qb < C::NQ2; ++qb) {
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
                 frag pf[C::NI];
                 to_bfrag<T>(pf, s[qb]);
 #pragma unroll
-                for (int i = 0; i < C::NI; ++i) *reinterpret_cast<frag *>(pw + qb * C::PBLK + i * C::KPL) = pf[i];
+                for (int i = 0; i < C::NI; ++i) *reinterpret_cast<frag *>(pw + qb * C::PBLK + i * (kWave * C::KPL)) = pf[i];
             }
         } else {
             // tile it-1: dP = dO V^T, dS = P o (dP - D), dK^T += Q^T dS
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
             for (int qb = 0; qb < C::NQ2; ++qb) {
                 frag pp[C::NI];
 #pragma unroll
-                for (int i = 0; i < C::NI; ++i) pp[i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * C::KPL);
+                for (int i = 0; i < C::NI; ++i) pp[i] = *reinterpret_cast<const frag *>(pr + qb * C::PBLK + i * (kWave * C::KPL));
                 f32x16 ds;  // -dS (Eq. 17)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {

@@ -145,118 +145,148 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
     issue(sK0, sV0, 0);
     issue(sK1, sV1, 1);
 
-    auto step = [&](const T *tK, const T *tV, T *nK, T *nV, int j) {
+    // The prefetch of a tile goes out one instruction at a time, spread over a
+    // step's work (parts: one before each S^T block and each O^T block).  It
+    // is issued unconditionally -- past the last tile its range is empty and
+    // it fetches nothing -- because a conditional issue makes the compiler
+    // wait for every DMA before the next LDS read.
+    constexpr int NP = 2 * C::NKB;
+    auto rs = C::DMA::range(k, 0, 0);  // range of the tile being prefetched
+    T *nT = sK2;                       // and the stage it lands in
+    auto part = [&](int p) {
+        if (p >= 0) dma.issue_part(p, NP, nT, rs, hw);
+    };
+    auto all_parts = [&]() {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) part(p);
+    };
+    // whether tile j holds any key this wave's queries may see
+    auto active = [&](int j) {
+        return j >= 0 && j < nkt && qw0 < S && !(causal && j * BK > qw0 + NQB * 32 - 1 + off);
+    };
+
+    // S^T of a tile, block (kb, qb): rows = keys j0 + 32*kb + ridx(r, h), col = query.
+    // Prefetch part p0 + kb goes out before key block kb (p0 < 0: none).
+    f32x16 s[NQB][C::NKB];
+    auto qk = [&](const T *tK, int p0) {
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            part(p0 < 0 ? -1 : p0 + kb);
+            // K fragments are read in groups of KG (each feeds NQB
+            // products; an odd count ends with a single one): with two
+            // query blocks per wave the registers would not hold them all
+            constexpr int KG = NQB > 1 ? 2 : C::NSD;
+            const T *krow = tK + (kb * 32 + rsigma(l32)) * C::DMA::PD::PITCH + h * (D / 2);
+            auto group = [&](auto n, int f0) {
+                constexpr int N = decltype(n)::value;
+                frag kf[N];
+                load_run<T, N>(kf, krow + f0 * C::KPL);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int st = 0; st < N; ++st) s[qb][kb] = M::run(kf[st], qf[qb][f0 + st], s[qb][kb]);
+            };
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x16{};
+#pragma unroll
+            for (int g = 0; g < C::NSD / KG; ++g) group(std::integral_constant<int, KG>{}, g * KG);
+            if constexpr (C::NSD % KG != 0)
+                group(std::integral_constant<int, C::NSD % KG>{}, C::NSD / KG * KG);
+        }
+    };
+    // mask, online softmax and row sums of tile j's scores (P left in s)
+    auto softmax = [&](int j) {
         const int j0 = j * BK;
-        wait_vmcnt<C::DMA::IPW>();  // this wave's part of tile j has landed (j+1 may be in flight)
-        lds_barrier();              // every part of tile j landed; stage of tile j-1 released
-        // Prefetch tile j+2 into the stage tile j-1 used, one instruction at
-        // a time spread over this step's work.  It is issued unconditionally
-        // -- past the last tile its range is empty and it fetches nothing --
-        // because a conditional issue makes the compiler wait for every DMA
-        // before the next LDS read.
-        // (parts: one before each S^T block and each O^T block)
-        constexpr int NP = 2 * C::NKB;
-        const auto rs = C::DMA::range(half ? v : k, (j + 2) * BK, Sk);
-        T *const nT = half ? nV : nK;
-        const bool active = qw0 < S && !(causal && j0 > qw0 + NQB * 32 - 1 + off);
-        if (!active) {
-            dma.issue(nT, half ? v : k, (j + 2) * BK, Sk, hw);
-        } else {
-            // S^T block (kb, qb): rows = keys j0 + 32*kb + ridx(r, h), col = query.
-            f32x16 s[NQB][C::NKB];
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-                dma.issue_part(kb, NP, nT, rs, hw);
-                // K fragments are read in groups of KG (each feeds NQB
-                // products; an odd count ends with a single one): with two
-                // query blocks per wave the registers would not hold them all
-                constexpr int KG = NQB > 1 ? 2 : C::NSD;
-                const T *krow = tK + (kb * 32 + rsigma(l32)) * C::DMA::PD::PITCH + h * (D / 2);
-                auto group = [&](auto n, int f0) {
-                    constexpr int N = decltype(n)::value;
-                    frag kf[N];
-                    load_run<T, N>(kf, krow + f0 * C::KPL);
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                        for (int st = 0; st < N; ++st) s[qb][kb] = M::run(kf[st], qf[qb][f0 + st], s[qb][kb]);
-                };
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = f32x16{};
-#pragma unroll
-                for (int g = 0; g < C::NSD / KG; ++g) group(std::integral_constant<int, KG>{}, g * KG);
-                if constexpr (C::NSD % KG != 0)
-                    group(std::integral_constant<int, C::NSD % KG>{}, C::NSD / KG * KG);
-            }
-            const bool need_mask = (causal && j0 + BK - 1 > qw0 + off) || (j0 + BK > Sk);
-            if (need_mask) {
-                // (the empty volatile asm keeps this block a real branch: only
-                // tiles crossing the diagonal or the sequence end pay for masking)
-                asm volatile("");
-                // key j0 + 32*kb + ridx(r, h) is kept iff it is below `lim`
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
-                    const int qi = qw0 + qb * 32 + l32;
-                    const int lim = causal ? min(qi + 1 + off, Sk) : Sk;
-                    const int t = lim - j0 - 2 * h;
-#pragma unroll
-                    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            s[qb][kb][r] = (32 * kb + ridx(r, 0) < t) ? s[qb][kb][r] : -INFINITY;
-                }
-            }
-            // Online softmax in base 2 (scores scaled by c = scale*log2 e).  The
-            // running maximum only moves when a score exceeds it by kRescaleSlack.
+        const bool need_mask = (causal && j0 + BK - 1 > qw0 + off) || (j0 + BK > Sk);
+        if (need_mask) {
+            // (the empty volatile asm keeps this block a real branch: only
+            // tiles crossing the diagonal or the sequence end pay for masking)
+            asm volatile("");
+            // key j0 + 32*kb + ridx(r, h) is kept iff it is below `lim`
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
-                float mx = -INFINITY;
+                const int qi = qw0 + qb * 32 + l32;
+                const int lim = causal ? min(qi + 1 + off, Sk) : Sk;
+                const int t = lim - j0 - 2 * h;
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-                mx = wave_xor32_max(mx) * c;
-                const bool grow = mx > mrow[qb] + kRescaleSlack;
-                if (__ballot(grow) != 0) {  // wave-uniform: rare after the first tile
-                    const float mnew = grow ? mx : mrow[qb];
-                    // (a row that has seen no key yet keeps -inf: its alpha is 1,
-                    // not exp2(-inf - -inf))
-                    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mrow[qb] - mnew);
-                    lrow[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
-                    mrow[qb] = mnew;
-                }
-                // a row whose maximum is still -inf has seen only masked keys: use 0
-                const float muse = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
-                float ps = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = fast_exp2(fmaf(s[qb][kb][r], c, -muse));
-                        s[qb][kb][r] = p;
-                        ps += p;
-                    }
-                lrow[qb] += ps;
+                    for (int r = 0; r < 16; ++r)
+                        s[qb][kb][r] = (32 * kb + ridx(r, 0) < t) ? s[qb][kb][r] : -INFINITY;
             }
-            // O^T += V^T P^T
+        }
+        // Online softmax in base 2 (scores scaled by c = scale*log2 e).  The
+        // running maximum only moves when a score exceeds it by kRescaleSlack.
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
-                dma.issue_part(C::NKB + kb, NP, nT, rs, hw);
-                frag pf[NQB][C::NI];
+        for (int qb = 0; qb < NQB; ++qb) {
+            float mx = -INFINITY;
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) to_bfrag<T>(pf[qb], s[qb][kb]);
+            for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                for (int db = 0; db < C::ND; ++db) {
-                    frag vf[C::NI];
-                    vt.load(vf, tV, kb, db);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+            mx = wave_xor32_max(mx) * c;
+            const bool grow = mx > mrow[qb] + kRescaleSlack;
+            if (__ballot(grow) != 0) {  // wave-uniform: rare after the first tile
+                const float mnew = grow ? mx : mrow[qb];
+                // (a row that has seen no key yet keeps -inf: its alpha is 1,
+                // not exp2(-inf - -inf))
+                const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mrow[qb] - mnew);
+                lrow[qb] *= alpha;
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                        for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(vf[i], pf[qb][i], acc[qb][db]);
-                }
+                for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
+                mrow[qb] = mnew;
             }
+            // a row whose maximum is still -inf has seen only masked keys: use 0
+            const float muse = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
+            float ps = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = fast_exp2(fmaf(s[qb][kb][r], c, -muse));
+                    s[qb][kb][r] = p;
+                    ps += p;
+                }
+            lrow[qb] += ps;
+        }
+    };
+    // O^T += V^T P^T; prefetch part p0 + kb goes out before key block kb (p0 < 0: none)
+    auto pv = [&](const T *tV, int p0) {
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            part(p0 < 0 ? -1 : p0 + kb);
+            frag pf[NQB][C::NI];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) to_bfrag<T>(pf[qb], s[qb][kb]);
+#pragma unroll
+            for (int db = 0; db < C::ND; ++db) {
+                frag vf[C::NI];
+                vt.load(vf, tV, kb, db);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(vf[i], pf[qb][i], acc[qb][db]);
+            }
+        }
+    };
+    // start of step j: tile j has landed everywhere, then tile j+2 is aimed at (nK, nV)
+    auto begin_step = [&](T *nK, T *nV, int j) {
+        wait_vmcnt<C::DMA::IPW>();  // this wave's part of tile j has landed (j+1 may be in flight)
+        lds_barrier();              // every part of it; the stage tile j+2 goes to is released
+        rs = C::DMA::range(half ? v : k, (j + 2) * BK, Sk);
+        nT = half ? nV : nK;
+    };
+
+    // Three stages: step j uses tile j, tile j+1 is in flight and tile j+2
+    // goes to the stage tile j-1 used.
+    auto step = [&](const T *tK, const T *tV, T *nK, T *nV, int j) {
+        begin_step(nK, nV, j);
+        if (!active(j)) {
+            all_parts();
+        } else {
+            qk(tK, 0);
+            softmax(j);
+            pv(tV, C::NKB);
         }
         wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
     };
