@@ -308,8 +308,17 @@ __device__ inline void store8(T *dst, const f32x16 &c, int r0, float mul) {
     }
 }
 
-__device__ inline float wave_xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ inline float wave_xor32_sum(float x) { return x + __shfl_xor(x, 32); }
+// Reductions over lane pairs (l, l ^ 32): the gfx950 half swap exchanges the
+// two 32-lane halves in registers (a shuffle would round-trip through LDS).
+// Swapping x with itself leaves each lane its own value and its partner's.
+__device__ inline float wave_xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float wave_xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
