@@ -15,6 +15,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Shape checks shared by every entry point.
 int check_shape(int B, int H, int S, int D, int dtype) {
     if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA_EINVAL;
+    if (S > (1 << 30)) return FA_EINVAL;  // tile positions (a few tiles past S) stay within int
     const long long bh = (long long)B * H;
     if (bh > 0x7fffffffLL) return FA_EINVAL;
     // elements per tensor must fit comfortably in 63 bits

@@ -33,7 +33,7 @@
  * Supported shapes.  D in {16, 32, 64, 80, 96, 128}; dtype FA_F32 or FA_BF16
  * (bf16 storage, bf16 matrix-core products with fp32 accumulation; the
  * softmax statistics, L and D are fp32).  scale must be finite and > 0.
- * B*H*S*D must fit in 63 bits; S < 2^31.
+ * B*H*S*D must fit in 63 bits; S <= 2^30 (tile positions stay within int).
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H

@@ -87,6 +87,7 @@ def _bwd(**kw):
     (dict(dtype=7), fa.FA_EUNSUPPORTED),
     (dict(q=MIS), fa.FA_EALIGN), (dict(o=MIS), fa.FA_EALIGN), (dict(lse=MIS), fa.FA_EALIGN),
     (dict(B=1 << 20, H=1 << 10, S=1 << 20, D=128), fa.FA_EINVAL),
+    (dict(S=(1 << 30) + 1, D=16), fa.FA_EINVAL),
 ])
 def test_fwd_rejects(lib, bad, code):
     assert _fwd(**bad) == code
@@ -104,7 +105,7 @@ def test_preprocess_rejects(lib, bad, code):
 @pytest.mark.parametrize("bad,code", [
     (dict(dq=None), fa.FA_EINVAL), (dict(delta=None), fa.FA_EINVAL), (dict(H=0), fa.FA_EINVAL),
     (dict(causal=-1), fa.FA_EINVAL), (dict(scale=float("-inf")), fa.FA_EINVAL),
-    (dict(D=100), fa.FA_EUNSUPPORTED), (dict(dtype=2), fa.FA_EUNSUPPORTED),
+    (dict(D=100), fa.FA_EUNSUPPORTED), (dict(dtype=2), fa.FA_EUNSUPPORTED), (dict(S=(1 << 30) + 64), fa.FA_EINVAL),
     (dict(dk=MIS), fa.FA_EALIGN), (dict(lse=P + 2), fa.FA_EALIGN),
 ])
 def test_bwd_rejects(lib, bad, code):

@@ -170,6 +170,28 @@ def test_workload_s65536_d128_sampled():
                    key_window=1024)
 
 
+@pytest.mark.slow
+def test_tensors_beyond_2_31_elements():
+    """65536 heads of 256 x 128: each tensor holds 2^31 elements (4 GiB in bf16), so the last
+    heads lie past every 32-bit element offset.  Heads at the start, middle and end of every
+    output are compared with the oracle element by element."""
+    dev = torch.device("cuda:0")
+    B, H, S, D = 1, 65536, 256, 128
+    assert B * H * S * D == 1 << 31
+    g = torch.Generator(device=dev).manual_seed(1500)
+    q, k, v, do = (torch.randn((B, H, S, D), device=dev, generator=g).to(torch.bfloat16)
+                   for _ in range(4))
+    print(f"[parity] 2^31-element tensors B={B} H={H} S={S} D={D}", flush=True)
+    o, lse = fa.forward(q, k, v, causal=True)
+    dq, dk, dv, delta = fa.backward(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    heads = [0, 1, H // 2, H - 2, H - 1]
+    pick = lambda t: t[:, heads].double().cpu().numpy()
+    r = oracle.backward(*(pick(x) for x in (q, k, v, do)), causal=True)
+    g_ = dict(o=pick(o), lse=pick(lse), dq=pick(dq), dk=pick(dk), dv=pick(dv), delta=pick(delta))
+    compare(g_, r, "bf16", "2^31 elements, heads " + str(heads))
+
+
 # ------------------------------------------------------ edges and tails ---
 
 @pytest.mark.parametrize("S", [1, 2, 15, 17, 31, 33, 63, 65, 127, 129, 200, 257])
