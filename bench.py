@@ -71,6 +71,9 @@ def parse():
                     help="only time the split-KV forward of the workload (fa_fwd_partial over N key "
                          "chunks, then fa_merge) and print its own JSON line: the partial forward "
                          "against the matrix-core peak, the merge against HBM bandwidth")
+    ap.add_argument("--vs-materialised", action="store_true",
+                    help="time and peak memory of fwd+bwd against attention with the S x S matrix "
+                         "materialised (fp32 PyTorch ops), batch 8, one head")
     ap.add_argument("--sweep", action="store_true",
                     help="only time the benchmark sweep (B=1, H=1, S = 128 .. 65536 in powers of "
                          "two, D in 16/32/64/128, bf16 and fp32, causal and not), print a "
@@ -266,6 +269,77 @@ def sweep(dev):
     return rows
 
 
+def vs_materialised(dev):
+    """One forward+backward of this library against attention with the S x S matrix materialised.
+
+    The comparator is the composed attention the pages benchmark first (scores, causal mask,
+    softmax and the value product as separate PyTorch ops on the GPU, differentiated by
+    autograd), in fp32.  Grid of the pages' attention benchmark: batch 8, one head,
+    D in {16, 32, 64, 128}, S in {256, ..., 16384}.  Times are medians of HIP-event times;
+    "peak MiB" is what one step allocates beyond its inputs (outputs and gradients included).
+    """
+    from exact_attention_causal_amd.inputs import make_inputs
+    fa.load_library()
+    stream = torch.cuda.current_stream(dev)
+    B, H = 8, 1
+
+    def measure(f, n=5):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        f()
+        torch.cuda.synchronize()
+        peak = (torch.cuda.max_memory_allocated() - base) / 2**20
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return statistics.median(x.elapsed_time(y) for x, y in ts), peak
+
+    print("| D | S | materialised fp32 fwd+bwd ms | materialised peak MiB | this library fp32 ms | "
+          "fp32 peak MiB | this library bf16 ms | bf16 peak MiB |")
+    print("|---|---|---|---|---|---|---|---|")
+    for D in (16, 32, 64, 128):
+        for S in (256, 1024, 4096, 8192, 16384):
+            scale = 1.0 / math.sqrt(D)
+            q, k, v, do = (x.to(dev) for x in make_inputs(B, H, S, D, "f32", seed=2000 + S + D))
+            mask = torch.ones((S, S), dtype=torch.bool, device=dev).triu(1)
+
+            def composed():
+                qg, kg, vg = (x.detach().requires_grad_(True) for x in (q, k, v))
+                sc = torch.matmul(qg, kg.transpose(-1, -2)) * scale
+                p = torch.softmax(sc.masked_fill(mask, float("-inf")), dim=-1)
+                torch.matmul(p, vg).backward(do)
+                return qg.grad, kg.grad, vg.grad
+
+            try:
+                t_m, m_m = measure(composed)
+                mat = f"{t_m:.3f} | {m_m:.1f}"
+            except torch.cuda.OutOfMemoryError:
+                mat = "OOM | OOM"
+            del mask
+            torch.cuda.empty_cache()
+            cells = []
+            for dt in (torch.float32, torch.bfloat16):
+                qd, kd, vd, dod = (x.to(dt) for x in (q, k, v, do))
+
+                def flash():
+                    o, lse = fa.forward(qd, kd, vd, causal=True, scale=scale)
+                    return fa.backward(qd, kd, vd, o, lse, dod, causal=True, scale=scale)
+
+                t_f, m_f = measure(flash)
+                cells.append(f"{t_f:.3f} | {m_f:.1f}")
+            print(f"| {D} | {S} | {mat} | {cells[0]} | {cells[1]} |", flush=True)
+            del q, k, v, do
+            torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -288,6 +362,9 @@ def main():
         return
     if args.sweep:
         sweep(dev)
+        return
+    if args.vs_materialised:
+        vs_materialised(dev)
         return
     if args.split_kv:
         split_kv(dev, WORKLOADS[args.workload], args.split_kv, args.steps, args.warmup,
