@@ -204,6 +204,8 @@ def sweep(dev):
                     lse = torch.empty((1, 1, S), device=dev, dtype=torch.float32)
                     delta = torch.empty_like(lse)
                     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                    ws_bytes = fa.fa_bwd_workspace_size(1, 1, S, D, code)
+                    ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
                     scale = 1.0 / math.sqrt(D)
 
                     def fwd():
@@ -214,7 +216,7 @@ def sweep(dev):
                         fwd()
                         rc = fa.fa_bwd_preprocess(o, do, delta, 1, 1, S, D, code, sh)
                         assert rc == 0, fa.fa_strerror(rc)
-                        rc = fa.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, None, 0, 1, 1, S, D,
+                        rc = fa.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, ws, ws_bytes, 1, 1, S, D,
                                        scale, causal, code, sh)
                         assert rc == 0, fa.fa_strerror(rc)
 
@@ -383,7 +385,7 @@ def main():
     delta = torch.empty_like(lse)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     ws_bytes = fa.fa_bwd_workspace_size(B, H, S, D, code)
-    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 

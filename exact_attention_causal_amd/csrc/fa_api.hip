@@ -62,12 +62,10 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int 
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype) {
-    (void)B;
-    (void)H;
-    (void)S;
-    (void)D;
-    (void)dtype;
-    return 0;
+    if (check_shape(B, H, S, D, dtype) != FA_OK) return 0;
+    // base-2 copy of lse: one fp32 per row
+    const size_t bytes = (size_t)B * H * S * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
@@ -77,13 +75,13 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const 
     if (causal != 0 && causal != 1) return FA_EINVAL;
     if (int rc = check_scale(scale)) return rc;
     if (int rc = check_shape(B, H, S, D, dtype)) return rc;
-    const void *ptrs[] = {q, k, v, dout, lse, delta, dq, dk, dv};
+    if (!workspace) return FA_EINVAL;
+    const void *ptrs[] = {q, k, v, dout, lse, delta, dq, dk, dv, workspace};
     for (const void *p : ptrs)
         if (!aligned16(p)) return FA_EALIGN;
     if (workspace_bytes < fa_bwd_workspace_size(B, H, S, D, dtype)) return FA_EWORKSPACE;
-    (void)workspace;
-    return map_launch(
-        fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv, B * H, S, D, scale, causal, stream));
+    return map_launch(fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv,
+                                     static_cast<float *>(workspace), B * H, S, D, scale, causal, stream));
 }
 
 int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, float *lse_parts,

@@ -66,6 +66,14 @@ __global__ __launch_bounds__(256) void delta_kernel(const T *__restrict__ o, con
     }
 }
 
+// L * log2(e) for every row, so that the two passes recompute
+// P = 2^(S * scale * log2 e - L * log2 e) with one FMA per probability.
+__global__ __launch_bounds__(256) void lse2_kernel(const float *__restrict__ lse, float *__restrict__ lse2,
+                                                   long long rows) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < rows) lse2[i] = lse[i] * kLog2e;
+}
+
 // --------------------------------------------------------- key-outer dK/dV ---
 //
 // Each 32-key block is owned by a pair of waves that split the block's four
@@ -85,9 +93,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const T *__restrict__ o, con
 // Problem shape of one backward launch.  Query i sits `off` positions after
 // key 0, so the causal mask allows key j iff j <= i + off (off = 0 and
 // Sq = Sk for self-attention).  With GEN = false (self-attention) the shift is
-// a compile-time zero and the gradients are written in the input dtype; with
-// GEN = true they are fp32 contributions of this key set, added to the
-// outputs when `accumulate` is set.  L and D are the statistics of the whole
+// a compile-time zero, the gradients are written in the input dtype and the
+// row statistic the kernels read is L * log2(e) (prepared once per launch);
+// with GEN = true they are fp32 contributions of this key set, added to the
+// outputs when `accumulate` is set, and the statistic is the natural-log L.  L and D are the statistics of the whole
 // attention, so a row with L = -inf allows no key of this set either: every
 // tile holding such a row crosses the causal boundary, and the mask zeroes
 // the row's P (the infinite exponential is selected away, never multiplied).
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 #pragma unroll
             for (int qb = 0; qb < C::NQ2; ++qb) {
                 float lv[16];
-                stat(lv, tQ, qb, kLog2e);
+                stat(lv, tQ, qb, GEN ? kLog2e : 1.f);  // (self-attention: already base 2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[qb][r] = fast_exp2(fmaf(s[qb][r], c, -lv[r]));  // Eq. 14
             }
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
         if (qi < S) {
             load_run<T, C::NSD>(qf[qb], q + (size_t)qi * D + h * (D / 2));
             load_run<T, C::NSD>(df[qb], dout + (size_t)qi * D + h * (D / 2));
-            lq[qb] = lse[qi] * kLog2e;
+            lq[qb] = GEN ? lse[qi] * kLog2e : lse[qi];  // (self-attention: already base 2)
             // a row without probability mass (L = -inf) gives P = 0
             if (GEN && lq[qb] == -INFINITY) lq[qb] = INFINITY;
             dl[qb] = delta[qi];
@@ -642,16 +651,21 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
 }
 
 int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
-               const float *lse, const float *delta, void *dq, void *dk, void *dv, int BH, int S,
-               int D, float scale, int causal, hipStream_t stream) {
+               const float *lse, const float *delta, void *dq, void *dk, void *dv, float *lse2, int BH,
+               int S, int D, float scale, int causal, hipStream_t stream) {
+    if (dtype != 0 && dtype != 1) return -2;
+    if (!head_dim_supported(D)) return -2;
+    const long long rows = (long long)BH * S;
+    const long long grid = (rows + 255) / 256;
+    if (grid > 0x7fffffffLL) return -1;
+    hipLaunchKernelGGL(lse2_kernel, dim3((unsigned)grid), dim3(256), 0, stream, lse, lse2, rows);
+    if (hipGetLastError() != hipSuccess) return -5;
     const BwdShape a{BH, S, S, 0, causal, 0, 0, scale * kLog2e, scale};
     if (dtype == 1)
-        return bwd_dispatch<bf16, bf16, false>(D, q, k, v, dout, lse, delta, (bf16 *)dq, (bf16 *)dk,
+        return bwd_dispatch<bf16, bf16, false>(D, q, k, v, dout, lse2, delta, (bf16 *)dq, (bf16 *)dk,
                                                (bf16 *)dv, a, stream);
-    if (dtype == 0)
-        return bwd_dispatch<float, float, false>(D, q, k, v, dout, lse, delta, (float *)dq, (float *)dk,
-                                                 (float *)dv, a, stream);
-    return -2;
+    return bwd_dispatch<float, float, false>(D, q, k, v, dout, lse2, delta, (float *)dq, (float *)dk,
+                                             (float *)dv, a, stream);
 }
 
 int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, const void *dout,

@@ -32,9 +32,10 @@ int launch_merge(int dtype, const float *o_parts, const float *lse_parts, int n,
 int launch_delta(int dtype, const void *o, const void *dout, float *delta, int BH, int S, int D,
                  hipStream_t stream);
 
+// lse2: BH*S floats of workspace for the base-2 copy of lse.
 int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
-               const float *lse, const float *delta, void *dq, void *dk, void *dv, int BH,
-               int S, int D, float scale, int causal, hipStream_t stream);
+               const float *lse, const float *delta, void *dq, void *dk, void *dv, float *lse2,
+               int BH, int S, int D, float scale, int causal, hipStream_t stream);
 
 // Gradient contributions of one key set (fp32, stored or added).
 int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, const void *dout,

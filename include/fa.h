@@ -20,7 +20,7 @@
  * keys share the length S and both start at position 0.
  *
  * Ownership.  The caller allocates every buffer (including the backward
- * workspace, if one is ever needed); the library never allocates, frees,
+ * workspace); the library never allocates, frees,
  * copies to or from the host, or synchronises.  Outputs are fully
  * overwritten; inputs must not alias outputs.  All pointers must be device
  * pointers aligned to 16 bytes.
@@ -80,10 +80,12 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
                       int B, int H, int S, int D, fa_dtype dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (0 = none; the
- * current backward needs none: dK/dV and dQ are each owned by one
- * workgroup, so no partial sums leave the chip).  Returns 0 for invalid
- * sizes as well; fa_bwd reports those.
+ * Bytes of device workspace fa_bwd needs for these sizes: B*H*S fp32 values
+ * (rounded up to 256 bytes), where fa_bwd keeps lse in base 2 (L * log2 e)
+ * so that recomputing P = 2^(S * scale * log2 e - L * log2 e) costs no
+ * multiply per probability.  No partial sums are kept there: dK/dV and dQ
+ * are each owned by one workgroup.  Returns 0 for invalid sizes; fa_bwd
+ * reports those.
  */
 size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
 
@@ -92,7 +94,11 @@ size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
  * probabilities recomputed from lse:
  *   q, k, v, dout : [B][H][S][D] inputs    lse, delta : [B][H][S] fp32 inputs
  *   dq, dk, dv    : [B][H][S][D] outputs
- *   workspace     : may be NULL when fa_bwd_workspace_size() is 0.
+ *   workspace     : device scratch of at least fa_bwd_workspace_size() bytes,
+ *                   16-byte aligned (FA_EWORKSPACE if smaller, FA_EINVAL if
+ *                   NULL); its contents on entry do not matter and are
+ *                   overwritten.  Calls that share one workspace must be
+ *                   ordered on one stream.
  * `scale` and `causal` must be the values the forward pass used.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *dout,

@@ -51,9 +51,13 @@ def test_strerror(lib):
     assert "unknown" in fa.fa_strerror(17)
 
 
-def test_workspace_size_is_zero(lib):
-    assert fa.fa_bwd_workspace_size(1, 16, 65536, 128, fa.FA_BF16) == 0
-    assert fa.fa_bwd_workspace_size(4, 12, 512, 64, fa.FA_F32) == 0
+def test_workspace_size(lib):
+    # one fp32 per row (the base-2 copy of lse), rounded up to 256 bytes; 0 for invalid sizes
+    assert fa.fa_bwd_workspace_size(1, 16, 65536, 128, fa.FA_BF16) == 16 * 65536 * 4
+    assert fa.fa_bwd_workspace_size(4, 12, 512, 64, fa.FA_F32) == 4 * 12 * 512 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64, fa.FA_BF16) == 256
+    assert fa.fa_bwd_workspace_size(1, 1, 0, 64, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 128, 72, fa.FA_BF16) == 0
 
 
 def _fwd(**kw):
@@ -70,8 +74,8 @@ def _pre(**kw):
 
 
 def _bwd(**kw):
-    a = dict(q=P, k=P, v=P, dout=P, lse=P, delta=P, dq=P, dk=P, dv=P, workspace=None,
-             workspace_bytes=0, B=1, H=2, S=128, D=64, scale=0.125, causal=1, dtype=fa.FA_BF16,
+    a = dict(q=P, k=P, v=P, dout=P, lse=P, delta=P, dq=P, dk=P, dv=P, workspace=P,
+             workspace_bytes=1 << 20, B=1, H=2, S=128, D=64, scale=0.125, causal=1, dtype=fa.FA_BF16,
              stream=0)
     a.update(kw)
     return fa.fa_bwd(**a)
@@ -107,6 +111,8 @@ def test_preprocess_rejects(lib, bad, code):
     (dict(causal=-1), fa.FA_EINVAL), (dict(scale=float("-inf")), fa.FA_EINVAL),
     (dict(D=100), fa.FA_EUNSUPPORTED), (dict(dtype=2), fa.FA_EUNSUPPORTED), (dict(S=(1 << 30) + 64), fa.FA_EINVAL),
     (dict(dk=MIS), fa.FA_EALIGN), (dict(lse=P + 2), fa.FA_EALIGN),
+    (dict(workspace=None), fa.FA_EINVAL), (dict(workspace=MIS), fa.FA_EALIGN),
+    (dict(workspace_bytes=2 * 128 * 4 - 1), fa.FA_EWORKSPACE), (dict(workspace_bytes=0), fa.FA_EWORKSPACE),
 ])
 def test_bwd_rejects(lib, bad, code):
     assert _bwd(**bad) == code
