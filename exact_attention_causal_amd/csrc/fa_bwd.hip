@@ -400,6 +400,223 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     }
 }
 
+// ----------------------------------------- key-outer dK/dV, one wave per key block ---
+//
+// The same pass with every 32-key block owned by a single wave that forms all
+// four products of a 32-query tile itself: S = Q K^T and P = 2^(S c - L)
+// (Eq. 13-14), dV^T += dO^T P (Eq. 15), D - dP = D - dO V^T (Eq. 16, V^T kept
+// negated, the chain started from D), -dS = P o (D - dP) (Eq. 17) and
+// -dK^T += Q^T (-dS) (Eq. 19).  P and dS go from the accumulator registers
+// straight into the next products (no LDS hand-off, no bf16 round trip of P
+// before dS), so the vector work per product is smaller than with pairs; the
+// price is both K^T and V^T and both accumulators in registers, which the
+// narrower head dimensions afford at two waves per SIMD.
+
+template <typename T, int D_, int NW_>
+struct KvTile1 {
+    static constexpr int D = D_, NW = NW_, NT = NW * kWave;
+    static constexpr int BQ = 32;                     // queries per step
+    static constexpr int BKV = NW * 32;               // keys per workgroup
+    static constexpr int KPL = Mma<T>::KPL;
+    static constexpr int NSD = D / 2 / KPL;
+    static constexpr int ND = (D + 31) / 32;
+    static constexpr int NI = 16 / KPL;
+    using DMA = TileDma<T, D, BQ, NW / 2>;           // half the waves load Q, half dO
+    // a Q (dO) tile array also carries the tile's L (D) values: 64 slots per
+    // loading wave (every wave issues the same number of loads per tile)
+    static constexpr int XOFF = DMA::ELEMS;
+    static constexpr int TILE = DMA::ELEMS + (NW / 2) * kWave * 4 / (int)sizeof(T);
+    static_assert(D % 16 == 0 && NW % 2 == 0, "tile shape");
+};
+
+template <typename T, typename C, typename OutT, bool GEN>
+__global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                      const T *__restrict__ v, const T *__restrict__ dout,
+                                                      const float *__restrict__ lse,
+                                                      const float *__restrict__ delta, OutT *__restrict__ dk,
+                                                      OutT *__restrict__ dv, BwdShape a) {
+    using M = Mma<T>;
+    using frag = typename M::frag;
+    constexpr int D = C::D;
+    // three stages of Q and dO tiles, each its own array (see the forward kernel)
+    __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE], sQ2[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE], sdO2[C::TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int BH = a.BH, S = a.Sq, causal = a.causal;
+    const int Sk = GEN ? a.Sk : S;
+    const int off = GEN ? a.off : 0;
+    const float c = a.c;
+    const int bid = blockIdx.x;
+    const int kt = bid / BH;  // ascending: the tiles with the most query tiles go first
+    const int bh = bid % BH;
+    q += (size_t)bh * S * D;
+    dout += (size_t)bh * S * D;
+    k += (size_t)bh * Sk * D;
+    v += (size_t)bh * Sk * D;
+    dk += (size_t)bh * Sk * D;
+    dv += (size_t)bh * Sk * D;
+    lse += (size_t)bh * S;
+    delta += (size_t)bh * S;
+    const int k0 = kt * C::BKV;
+    const int kw0 = k0 + wave * 32;
+    const int key = kw0 + l32;  // this lane's key column
+
+    // B operands: K^T and -V^T (the dP chain then yields D - dP)
+    frag bk[C::NSD], bv[C::NSD];
+    if (key < Sk) {
+        load_run<T, C::NSD>(bk, k + (size_t)key * D + h * (D / 2));
+        load_run<T, C::NSD>(bv, v + (size_t)key * D + h * (D / 2));
+    } else {
+        zero_run<T, C::NSD>(bk);
+        zero_run<T, C::NSD>(bv);
+    }
+    neg_run<T, C::NSD>(bv);
+    TransReader<T, D> tr;
+    tr.init(lane);
+
+    f32x16 accV[C::ND], accK[C::ND];  // dV^T and -dK^T
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db) {
+        accV[db] = f32x16{};
+        accK[db] = f32x16{};
+    }
+
+    const int nq = (S + C::BQ - 1) / C::BQ;
+    const int i0 = !causal ? 0
+                   : GEN   ? __builtin_amdgcn_readfirstlane(min(max(0, k0 - off) / C::BQ, nq))
+                           : k0 / C::BQ;
+
+    typename C::DMA dma;
+    const int half = wave / (C::NW / 2), hw = wave % (C::NW / 2);
+    dma.init(lane, hw);
+    typedef __attribute__((address_space(3))) void lds_void;
+    // slot j of a wave's statistics holds the query that a lane half reads as
+    // registers of its 32-query block: slot 16u + 8h + 4rr + e <-> query
+    // ridx(8u + 4rr + e, h) (lanes 32..63 repeat lanes 0..31)
+    const int jq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
+    auto issue = [&](T *nQ, T *ndO, int it) {
+        T *dst = half ? ndO : nQ;
+        dma.issue(dst, half ? dout : q, it * C::BQ, S, hw);
+        const int qi = min(it * C::BQ + jq, S - 1);
+        __builtin_amdgcn_global_load_lds((const void *)((half ? delta : lse) + qi),
+                                         (lds_void *)(dst + C::XOFF + hw * kWave * 4 / (int)sizeof(T)), 4, 0, 0);
+    };
+    // this wave's L (from a Q tile) or D (from a dO tile) for its 16 rows
+    auto stat = [&](float (&x)[16], const T *tile, float mul) {
+        const float *wX = reinterpret_cast<const float *>(tile + C::XOFF) + hw * kWave;
+#pragma unroll
+        for (int hr = 0; hr < 2; ++hr) {
+            const int base = 16 * hr + 8 * h;
+            const f32x4 p0 = *reinterpret_cast<const f32x4 *>(wX + base);
+            const f32x4 p1 = *reinterpret_cast<const f32x4 *>(wX + base + 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x[8 * hr + t] = p0[t] * mul;
+                x[8 * hr + 4 + t] = p1[t] * mul;
+            }
+        }
+    };
+    issue(sQ0, sdO0, i0);
+    issue(sQ1, sdO1, i0 + 1);
+
+    auto step = [&](const T *tQ, const T *tdO, T *nQ, T *ndO, int it) {
+        const int q0 = it * C::BQ;
+        wait_vmcnt<C::DMA::IPW + 1>();  // this wave's part of tile it has landed (it+1 may be in flight)
+        lds_barrier();                  // every part of it; the stage of tile it-1 is released
+        issue(nQ, ndO, it + 2);         // unconditionally (see the forward kernel)
+        const bool active = !(causal && kw0 > q0 + C::BQ - 1 + off);
+        if (active) {
+            // S block: rows = queries q0 + ridx(r, h), col = key; P = 2^(S c - L)
+            f32x16 s = f32x16{};
+            {
+                frag qa[C::NSD];
+                load_row_frags<T, D>(qa, tQ, rsigma(l32), h);
+#pragma unroll
+                for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], bk[st], s);
+            }
+            {
+                float lv[16];
+                stat(lv, tQ, GEN ? kLog2e : 1.f);  // (self-attention: already base 2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
+            }
+            const bool need_mask = (causal && kw0 + 31 > q0 + off) || (q0 + C::BQ > S);
+            if (need_mask) {
+                asm volatile("");  // a real branch: only diagonal / tail tiles pay for masking
+                // query q0 + ridx(r, h) is kept iff it is at least `lo` and below `hi`
+                const int lo = (causal ? key - off : 0) - q0 - 2 * h;
+                const int hi = S - q0 - 2 * h;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int e = ridx(r, 0);
+                    s[r] = (e >= lo && e < hi) ? s[r] : 0.f;
+                }
+            }
+            // dV^T += dO^T P (Eq. 15)
+            {
+                frag pf[C::NI];
+                to_bfrag<T>(pf, s);
+#pragma unroll
+                for (int db = 0; db < C::ND; ++db) {
+                    frag at[C::NI];
+                    tr.load(at, tdO, 0, db);
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) accV[db] = M::run(at[i], pf[i], accV[db]);
+                }
+            }
+            // D - dP (Eq. 16), then -dS = P o (D - dP) (Eq. 17)
+            f32x16 dp;
+            {
+                float dl[16];
+                stat(dl, tdO, 1.f);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dp[r] = dl[r];
+                frag da[C::NSD];
+                load_row_frags<T, D>(da, tdO, rsigma(l32), h);
+#pragma unroll
+                for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bv[st], dp);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[r] *= s[r];
+            // -dK^T += Q^T (-dS) (Eq. 19)
+            {
+                frag sf[C::NI];
+                to_bfrag<T>(sf, dp);
+#pragma unroll
+                for (int db = 0; db < C::ND; ++db) {
+                    frag at[C::NI];
+                    tr.load(at, tQ, 0, db);
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) accK[db] = M::run(at[i], sf[i], accK[db]);
+                }
+            }
+        }
+        wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
+    };
+    for (int it = i0; it < nq; it += 3) {
+        step(sQ0, sdO0, sQ2, sdO2, it);
+        if (it + 1 < nq) step(sQ1, sdO1, sQ0, sdO0, it + 1);
+        if (it + 2 < nq) step(sQ2, sdO2, sQ1, sdO1, it + 2);
+    }
+    wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it exits
+
+    if (key < Sk) {
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr) {
+                const int d0 = db * 32 + 16 * hr + 8 * h;
+                if (d0 < D) {
+                    out8<GEN>(dv + (size_t)key * D + d0, accV[db], 8 * hr, 1.f, a.accumulate);
+                    out8<GEN>(dk + (size_t)key * D + d0, accK[db], 8 * hr, -a.scale, a.accumulate);
+                }
+            }
+    }
+}
+
 // -------------------------------------------------------- query-outer dQ ---
 
 template <typename T, int D_, int NQB_, int BK_, int NW_>
@@ -601,18 +818,32 @@ template <typename T, int D>
 using KvTileFor = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
 template <typename T, int D>
 using QTileFor = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
+template <typename T, int D>
+using KvTile1For = KvTile1<T, D, 8>;
+// dK/dV with one wave per key block where the registers hold both operands
+// and both accumulators without spilling (bf16 up to D = 96: 6 % faster at
+// D = 80, 10 % at D = 64 than pairs); pairs of waves otherwise (at D = 128 the
+// single-wave kernel spills and is 19 % slower)
+template <typename T, int D>
+constexpr bool kv_single() { return sizeof(T) == 2 && D <= 96; }
 
 template <typename T, int D, typename OutT, bool GEN>
 static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                    const float *delta, OutT *dq, OutT *dk, OutT *dv, BwdShape a, hipStream_t stream) {
     using KC = KvTileFor<T, D>;
+    using K1 = KvTile1For<T, D>;
     using QC = QTileFor<T, D>;
-    const long long g1 = (long long)((a.Sk + KC::BKV - 1) / KC::BKV) * a.BH;
+    constexpr int BKV = kv_single<T, D>() ? K1::BKV : KC::BKV;
+    const long long g1 = (long long)((a.Sk + BKV - 1) / BKV) * a.BH;
     a.nqt = (a.Sq + QC::BQ - 1) / QC::BQ;
     const long long g2 = (long long)a.nqt * a.BH;
     if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
-    hipLaunchKernelGGL((dkdv_kernel<T, KC, OutT, GEN>), dim3((unsigned)g1), dim3(KC::NT), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dk, dv, a);
+    if constexpr (kv_single<T, D>())
+        hipLaunchKernelGGL((dkdv1_kernel<T, K1, OutT, GEN>), dim3((unsigned)g1), dim3(K1::NT), 0, stream,
+                           (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dk, dv, a);
+    else
+        hipLaunchKernelGGL((dkdv_kernel<T, KC, OutT, GEN>), dim3((unsigned)g1), dim3(KC::NT), 0, stream,
+                           (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dk, dv, a);
     if (hipGetLastError() != hipSuccess) return -5;
     hipLaunchKernelGGL((dq_kernel<T, QC, OutT, GEN>), dim3((unsigned)g2), dim3(QC::NT), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dq, a);
@@ -687,7 +918,9 @@ int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, c
     template __global__ void dkdv_kernel<T, KvTileFor<T, D>, OUT, GEN>(                                     \
         const T *, const T *, const T *, const T *, const float *, const float *, OUT *, OUT *, BwdShape);  \
     template __global__ void dq_kernel<T, QTileFor<T, D>, OUT, GEN>(                                        \
-        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, BwdShape);
+        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, BwdShape);  \
+    template __global__ void dkdv1_kernel<T, KvTile1For<T, D>, OUT, GEN>(                                   \
+        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, OUT *, BwdShape);
 #define FA_BWD_HEAD(T, D)                 \
     FA_BWD_KERNELS(T, D, T, false)        \
     FA_BWD_KERNELS(T, D, float, true)
