@@ -412,9 +412,12 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 // price is both K^T and V^T and both accumulators in registers, which the
 // narrower head dimensions afford at two waves per SIMD.
 
-template <typename T, int D_, int NW_>
+template <typename T, int D_, int NW_, bool VLDS_ = false>
 struct KvTile1 {
     static constexpr int D = D_, NW = NW_, NT = NW * kWave;
+    // -V^T read from LDS every step (written there once) instead of held in
+    // registers: 4 * D / (16 / KPL) fewer registers per lane
+    static constexpr bool VLDS = VLDS_;
     static constexpr int BQ = 32;                     // queries per step
     static constexpr int BKV = NW * 32;               // keys per workgroup
     static constexpr int KPL = Mma<T>::KPL;
@@ -441,6 +444,8 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     // three stages of Q and dO tiles, each its own array (see the forward kernel)
     __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE], sQ2[C::TILE];
     __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE], sdO2[C::TILE];
+    using PD = typename C::DMA::PD;
+    __shared__ __attribute__((aligned(16))) T sV[C::VLDS ? C::BKV * PD::PITCH : 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -465,15 +470,29 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     const int key = kw0 + l32;  // this lane's key column
 
     // B operands: K^T and -V^T (the dP chain then yields D - dP)
-    frag bk[C::NSD], bv[C::NSD];
+    frag bk[C::NSD], bv[C::VLDS ? 1 : C::NSD];
+    // this lane's -V^T run in LDS (its own row: no other wave reads it)
+    T *const sVl = sV + (C::VLDS ? (wave * 32 + l32) * PD::PITCH + h * (D / 2) : 0);
     if (key < Sk) {
         load_run<T, C::NSD>(bk, k + (size_t)key * D + h * (D / 2));
-        load_run<T, C::NSD>(bv, v + (size_t)key * D + h * (D / 2));
     } else {
         zero_run<T, C::NSD>(bk);
-        zero_run<T, C::NSD>(bv);
     }
-    neg_run<T, C::NSD>(bv);
+    {
+        frag vt0[C::NSD];
+        if (key < Sk)
+            load_run<T, C::NSD>(vt0, v + (size_t)key * D + h * (D / 2));
+        else
+            zero_run<T, C::NSD>(vt0);
+        neg_run<T, C::NSD>(vt0);
+        if constexpr (C::VLDS) {
+#pragma unroll
+            for (int i = 0; i < C::NSD; ++i) *reinterpret_cast<frag *>(sVl + i * C::KPL) = vt0[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::NSD; ++i) bv[i] = vt0[i];
+        }
+    }
     TransReader<T, D> tr;
     tr.init(lane);
 
@@ -576,8 +595,15 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
                 for (int r = 0; r < 16; ++r) dp[r] = dl[r];
                 frag da[C::NSD];
                 load_row_frags<T, D>(da, tdO, rsigma(l32), h);
+                if constexpr (C::VLDS) {
+                    frag bvl[C::NSD];
+                    load_run<T, C::NSD>(bvl, sVl);
 #pragma unroll
-                for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bv[st], dp);
+                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bvl[st], dp);
+                } else {
+#pragma unroll
+                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bv[st], dp);
+                }
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) dp[r] *= s[r];
@@ -818,14 +844,14 @@ template <typename T, int D>
 using KvTileFor = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
 template <typename T, int D>
 using QTileFor = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
+// (bf16 D = 128 keeps -V^T in LDS: with it in registers the kernel spills)
 template <typename T, int D>
-using KvTile1For = KvTile1<T, D, 8>;
-// dK/dV with one wave per key block where the registers hold both operands
-// and both accumulators without spilling (bf16 up to D = 96: 6 % faster at
-// D = 80, 10 % at D = 64 than pairs); pairs of waves otherwise (at D = 128 the
-// single-wave kernel spills and is 19 % slower)
+using KvTile1For = KvTile1<T, D, 8, sizeof(T) == 2 && D == 128>;
+// dK/dV with one wave per key block for bf16 (faster than pairs by 6 % at
+// D = 80, 10 % at D = 64 and 5 % at D = 128); pairs of waves for fp32, whose
+// wider fragments do not fit two waves per SIMD with both operands held
 template <typename T, int D>
-constexpr bool kv_single() { return sizeof(T) == 2 && D <= 96; }
+constexpr bool kv_single() { return sizeof(T) == 2; }
 
 template <typename T, int D, typename OutT, bool GEN>
 static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
