@@ -412,13 +412,14 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 // price is both K^T and V^T and both accumulators in registers, which the
 // narrower head dimensions afford at two waves per SIMD.
 
-template <typename T, int D_, int NW_, bool VLDS_ = false>
+template <typename T, int D_, int NW_, bool VLDS_ = false, int NQB_ = 1>
 struct KvTile1 {
     static constexpr int D = D_, NW = NW_, NT = NW * kWave;
+    static constexpr int NQB = NQB_;                  // 32-query blocks per step
     // -V^T read from LDS every step (written there once) instead of held in
     // registers: 4 * D / (16 / KPL) fewer registers per lane
     static constexpr bool VLDS = VLDS_;
-    static constexpr int BQ = 32;                     // queries per step
+    static constexpr int BQ = 32 * NQB;               // queries per step
     static constexpr int BKV = NW * 32;               // keys per workgroup
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;
@@ -429,7 +430,7 @@ struct KvTile1 {
     // loading wave (every wave issues the same number of loads per tile)
     static constexpr int XOFF = DMA::ELEMS;
     static constexpr int TILE = DMA::ELEMS + (NW / 2) * kWave * 4 / (int)sizeof(T);
-    static_assert(D % 16 == 0 && NW % 2 == 0, "tile shape");
+    static_assert(D % 16 == 0 && NW % 2 == 0 && (NQB == 1 || NQB == 2), "tile shape");
 };
 
 template <typename T, typename C, typename OutT, bool GEN>
@@ -513,9 +514,11 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     dma.init(lane, hw);
     typedef __attribute__((address_space(3))) void lds_void;
     // slot j of a wave's statistics holds the query that a lane half reads as
-    // registers of its 32-query block: slot 16u + 8h + 4rr + e <-> query
-    // ridx(8u + 4rr + e, h) (lanes 32..63 repeat lanes 0..31)
-    const int jq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
+    // registers of its 32-query block: slot 32b + 16u + 8h + 4rr + e <->
+    // query 32b + ridx(8u + 4rr + e, h) (with one block per tile, lanes
+    // 32..63 repeat lanes 0..31)
+    const int jq = (C::NQB > 1 ? 32 * (lane >> 5) : 0) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3) +
+                   2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
     auto issue = [&](T *nQ, T *ndO, int it) {
         T *dst = half ? ndO : nQ;
         dma.issue(dst, half ? dout : q, it * C::BQ, S, hw);
@@ -523,12 +526,12 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
         __builtin_amdgcn_global_load_lds((const void *)((half ? delta : lse) + qi),
                                          (lds_void *)(dst + C::XOFF + hw * kWave * 4 / (int)sizeof(T)), 4, 0, 0);
     };
-    // this wave's L (from a Q tile) or D (from a dO tile) for its 16 rows
-    auto stat = [&](float (&x)[16], const T *tile, float mul) {
+    // this wave's L (from a Q tile) or D (from a dO tile) for its 16 rows of block qb
+    auto stat = [&](float (&x)[16], const T *tile, int qb, float mul) {
         const float *wX = reinterpret_cast<const float *>(tile + C::XOFF) + hw * kWave;
 #pragma unroll
         for (int hr = 0; hr < 2; ++hr) {
-            const int base = 16 * hr + 8 * h;
+            const int base = 32 * qb + 16 * hr + 8 * h;
             const f32x4 p0 = *reinterpret_cast<const f32x4 *>(wX + base);
             const f32x4 p1 = *reinterpret_cast<const f32x4 *>(wX + base + 4);
 #pragma unroll
@@ -546,28 +549,30 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
         wait_vmcnt<C::DMA::IPW + 1>();  // this wave's part of tile it has landed (it+1 may be in flight)
         lds_barrier();                  // every part of it; the stage of tile it-1 is released
         issue(nQ, ndO, it + 2);         // unconditionally (see the forward kernel)
-        const bool active = !(causal && kw0 > q0 + C::BQ - 1 + off);
-        if (active) {
-            // S block: rows = queries q0 + ridx(r, h), col = key; P = 2^(S c - L)
+        // one 32-query block: queries q0 + 32*qb + ridx(r, h)
+        auto block = [&](int qb) {
+            const int qb0 = q0 + 32 * qb;
+            if (causal && kw0 > qb0 + 31 + off) return;  // no key of this wave is visible yet
+            // S block: rows = queries qb0 + ridx(r, h), col = key; P = 2^(S c - L)
             f32x16 s = f32x16{};
             {
                 frag qa[C::NSD];
-                load_row_frags<T, D>(qa, tQ, rsigma(l32), h);
+                load_row_frags<T, D>(qa, tQ, 32 * qb + rsigma(l32), h);
 #pragma unroll
                 for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], bk[st], s);
             }
             {
                 float lv[16];
-                stat(lv, tQ, GEN ? kLog2e : 1.f);  // (self-attention: already base 2)
+                stat(lv, tQ, qb, GEN ? kLog2e : 1.f);  // (self-attention: already base 2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lv[r]));  // Eq. 14
             }
-            const bool need_mask = (causal && kw0 + 31 > q0 + off) || (q0 + C::BQ > S);
+            const bool need_mask = (causal && kw0 + 31 > qb0 + off) || (qb0 + 32 > S);
             if (need_mask) {
                 asm volatile("");  // a real branch: only diagonal / tail tiles pay for masking
-                // query q0 + ridx(r, h) is kept iff it is at least `lo` and below `hi`
-                const int lo = (causal ? key - off : 0) - q0 - 2 * h;
-                const int hi = S - q0 - 2 * h;
+                // query qb0 + ridx(r, h) is kept iff it is at least `lo` and below `hi`
+                const int lo = (causal ? key - off : 0) - qb0 - 2 * h;
+                const int hi = S - qb0 - 2 * h;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int e = ridx(r, 0);
@@ -581,7 +586,7 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
 #pragma unroll
                 for (int db = 0; db < C::ND; ++db) {
                     frag at[C::NI];
-                    tr.load(at, tdO, 0, db);
+                    tr.load(at, tdO, qb, db);
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) accV[db] = M::run(at[i], pf[i], accV[db]);
                 }
@@ -590,11 +595,11 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
             f32x16 dp;
             {
                 float dl[16];
-                stat(dl, tdO, 1.f);
+                stat(dl, tdO, qb, 1.f);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dp[r] = dl[r];
                 frag da[C::NSD];
-                load_row_frags<T, D>(da, tdO, rsigma(l32), h);
+                load_row_frags<T, D>(da, tdO, 32 * qb + rsigma(l32), h);
                 if constexpr (C::VLDS) {
                     frag bvl[C::NSD];
                     load_run<T, C::NSD>(bvl, sVl);
@@ -614,12 +619,14 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
 #pragma unroll
                 for (int db = 0; db < C::ND; ++db) {
                     frag at[C::NI];
-                    tr.load(at, tQ, 0, db);
+                    tr.load(at, tQ, qb, db);
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) accK[db] = M::run(at[i], sf[i], accK[db]);
                 }
             }
-        }
+        };
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) block(qb);
         wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
     };
     for (int it = i0; it < nq; it += 3) {
@@ -844,9 +851,11 @@ template <typename T, int D>
 using KvTileFor = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
 template <typename T, int D>
 using QTileFor = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
-// (bf16 D = 128 keeps -V^T in LDS: with it in registers the kernel spills)
+// (bf16 D = 128 keeps -V^T in LDS: with it in registers the kernel spills;
+// up to D = 96 two 32-query blocks per step halve the barriers and DMA issues
+// per product, 4-5 % faster; at D = 128 the LDS would not hold them)
 template <typename T, int D>
-using KvTile1For = KvTile1<T, D, 8, sizeof(T) == 2 && D == 128>;
+using KvTile1For = KvTile1<T, D, 8, sizeof(T) == 2 && D == 128, (sizeof(T) == 2 && D <= 96) ? 2 : 1>;
 // dK/dV with one wave per key block for bf16 (faster than pairs by 6 % at
 // D = 80, 10 % at D = 64 and 5 % at D = 128); pairs of waves for fp32, whose
 // wider fragments do not fit two waves per SIMD with both operands held
