@@ -412,10 +412,12 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 // price is both K^T and V^T and both accumulators in registers, which the
 // narrower head dimensions afford at two waves per SIMD.
 
-template <typename T, int D_, int NW_, bool VLDS_ = false, int NQB_ = 1>
+template <typename T, int D_, int NW_, bool VLDS_ = false, int NQB_ = 1, int NSTAGE_ = 3>
 struct KvTile1 {
     static constexpr int D = D_, NW = NW_, NT = NW * kWave;
     static constexpr int NQB = NQB_;                  // 32-query blocks per step
+    // LDS stages of Q/dO tiles: 3 (two tiles in flight) or 2 (one)
+    static constexpr int NSTAGE = NSTAGE_;
     // -V^T read from LDS every step (written there once) instead of held in
     // registers: 4 * D / (16 / KPL) fewer registers per lane
     static constexpr bool VLDS = VLDS_;
@@ -431,6 +433,7 @@ struct KvTile1 {
     static constexpr int XOFF = DMA::ELEMS;
     static constexpr int TILE = DMA::ELEMS + (NW / 2) * kWave * 4 / (int)sizeof(T);
     static_assert(D % 16 == 0 && NW % 2 == 0 && (NQB == 1 || NQB == 2), "tile shape");
+    static_assert(NSTAGE == 2 || NSTAGE == 3, "stages");
 };
 
 template <typename T, typename C, typename OutT, bool GEN>
@@ -442,9 +445,10 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     using M = Mma<T>;
     using frag = typename M::frag;
     constexpr int D = C::D;
-    // three stages of Q and dO tiles, each its own array (see the forward kernel)
-    __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE], sQ2[C::TILE];
-    __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE], sdO2[C::TILE];
+    // two or three stages of Q and dO tiles, each its own array (see the forward kernel)
+    constexpr int T3 = C::NSTAGE == 3 ? C::TILE : 8;
+    __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE], sQ2[T3];
+    __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE], sdO2[T3];
     using PD = typename C::DMA::PD;
     __shared__ __attribute__((aligned(16))) T sV[C::VLDS ? C::BKV * PD::PITCH : 8];
 
@@ -542,13 +546,19 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
         }
     };
     issue(sQ0, sdO0, i0);
-    issue(sQ1, sdO1, i0 + 1);
+    if constexpr (C::NSTAGE == 3) issue(sQ1, sdO1, i0 + 1);
 
     auto step = [&](const T *tQ, const T *tdO, T *nQ, T *ndO, int it) {
         const int q0 = it * C::BQ;
-        wait_vmcnt<C::DMA::IPW + 1>();  // this wave's part of tile it has landed (it+1 may be in flight)
-        lds_barrier();                  // every part of it; the stage of tile it-1 is released
-        issue(nQ, ndO, it + 2);         // unconditionally (see the forward kernel)
+        if constexpr (C::NSTAGE == 3) {
+            wait_vmcnt<C::DMA::IPW + 1>();  // this wave's part of tile it has landed (it+1 may be in flight)
+            lds_barrier();                  // every part of it; the stage of tile it-1 is released
+            issue(nQ, ndO, it + 2);         // unconditionally (see the forward kernel)
+        } else {
+            wait_vmcnt<0>();  // this wave's part of tile it has landed
+            lds_barrier();    // every part of it; the other stage (tile it-1) is released
+            issue(nQ, ndO, it + 1);
+        }
         // one 32-query block: queries q0 + 32*qb + ridx(r, h)
         auto block = [&](int qb) {
             const int qb0 = q0 + 32 * qb;
@@ -629,10 +639,17 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
         for (int qb = 0; qb < C::NQB; ++qb) block(qb);
         wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
     };
-    for (int it = i0; it < nq; it += 3) {
-        step(sQ0, sdO0, sQ2, sdO2, it);
-        if (it + 1 < nq) step(sQ1, sdO1, sQ0, sdO0, it + 1);
-        if (it + 2 < nq) step(sQ2, sdO2, sQ1, sdO1, it + 2);
+    if constexpr (C::NSTAGE == 3) {
+        for (int it = i0; it < nq; it += 3) {
+            step(sQ0, sdO0, sQ2, sdO2, it);
+            if (it + 1 < nq) step(sQ1, sdO1, sQ0, sdO0, it + 1);
+            if (it + 2 < nq) step(sQ2, sdO2, sQ1, sdO1, it + 2);
+        }
+    } else {
+        for (int it = i0; it < nq; it += 2) {
+            step(sQ0, sdO0, sQ1, sdO1, it);
+            if (it + 1 < nq) step(sQ1, sdO1, sQ0, sdO0, it + 1);
+        }
     }
     wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it exits
 
@@ -851,11 +868,13 @@ template <typename T, int D>
 using KvTileFor = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
 template <typename T, int D>
 using QTileFor = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
-// (bf16 D = 128 keeps -V^T in LDS: with it in registers the kernel spills;
-// up to D = 96 two 32-query blocks per step halve the barriers and DMA issues
-// per product, 4-5 % faster; at D = 128 the LDS would not hold them)
+// (bf16 D = 128 keeps -V^T in LDS: with it in registers the kernel spills.
+// Two 32-query blocks per step halve the barriers and DMA issues per
+// product: 4-5 % faster up to D = 96; at D = 128 the LDS holds them beside
+// -V^T only with two stages (1 % faster than one block with three).)
 template <typename T, int D>
-using KvTile1For = KvTile1<T, D, 8, sizeof(T) == 2 && D == 128, (sizeof(T) == 2 && D <= 96) ? 2 : 1>;
+using KvTile1For = KvTile1<T, D, 8, sizeof(T) == 2 && D == 128, sizeof(T) == 2 ? 2 : 1,
+                           (sizeof(T) == 2 && D == 128) ? 2 : 3>;
 // dK/dV with one wave per key block for bf16 (faster than pairs by 6 % at
 // D = 80, 10 % at D = 64 and 5 % at D = 128); pairs of waves for fp32, whose
 // wider fragments do not fit two waves per SIMD with both operands held
