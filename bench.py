@@ -482,7 +482,7 @@ def main():
                      "traffic": (FWD_TRAFFIC["bytes"] if w.name == DEFAULT_WORKLOAD
                                  and FWD_TRAFFIC["sources_sha1"] == fwd_sources_sha1() else None),
                      "algorithmic_per_launch": {"flop": f_fwd, "bytes": 4 * tensor + 4 * B * H * S}},
-        "roofline_bwd": {"kernel": "dkdv_kernel + dq_kernel (fa_bwd)", "bound": "mfma",
+        "roofline_bwd": {"kernel": "dK/dV + dQ kernels (fa_bwd)", "bound": "mfma",
                          "achieved": round(bwd_tf, 2), "peak": peak, "unit": "TFLOP/s",
                          "frac": round(bwd_tf / peak, 4)},
     }
