@@ -4,14 +4,14 @@
 // Eq. 13-19: the probabilities are recomputed from the saved logsumexp,
 // P_ij = exp(S_ij - L_i), with the per-query statistic
 // D_i = rowsum(O o dO) computed beforehand, and the work is split into
-//   * a key/value-outer pass: one workgroup per tile of 128 keys (32 per
-//     wave) accumulates dV = P^T dO and dK = dS^T Q * scale over the query
-//     tiles at or below the diagonal;
+//   * a key/value-outer pass: one workgroup per tile of keys (32 per wave,
+//     or per pair of waves for fp32) accumulates dV = P^T dO and
+//     dK = dS^T Q * scale over the query tiles at or below the diagonal;
 //   * a query-outer pass: one workgroup per tile of queries accumulates
 //     dQ = dS K * scale over the key tiles at or before the diagonal.
 // P (and dS) are computed twice, once in each pass, so no partial sums ever
-// cross workgroups: no atomics, no workspace, bit-reproducible results (the
-// handout's argument for Algorithm 2).
+// cross workgroups: no atomics, bit-reproducible results (the handout's
+// argument for Algorithm 2).  The only workspace is a base-2 copy of L.
 //
 // Register/LDS mapping (see fa_common.hpp): in the key-outer pass the scores
 // are formed as S = Q K^T so that each lane owns one key column; P and dS
