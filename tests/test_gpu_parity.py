@@ -201,6 +201,15 @@ def test_sequence_tails(S, dtype):
     check_full(q, k, v, do, dtype, causal=True, label=f"tail S={S}")
 
 
+@pytest.mark.parametrize("S", [1, 31, 65, 129, 255, 257, 511])
+@pytest.mark.parametrize("D", [80, 128])
+def test_sequence_tails_wide_heads(S, D):
+    # ragged query tiles (64 rows) and key tiles (256 keys) of the bf16 key-outer pass at the
+    # head dims with their own tilings (D = 128: -V^T in LDS, two stages)
+    q, k, v, do = make_inputs(1, 2, S, D, "bf16", seed=1600 + S + D)
+    check_full(q, k, v, do, "bf16", causal=True, label=f"tail S={S} D={D}")
+
+
 @pytest.mark.parametrize("D", [16, 32, 64, 80, 96, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_head_dims(D, dtype):
