@@ -495,6 +495,60 @@ def test_ring_schedule_matches_full_attention(S, R, D, skip_masked):
         assert errs[n] <= TOL["bf16"]["grad"], (n, errs)
 
 
+def _random_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    for _ in range(n):
+        yield dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), S=int(rng.integers(1, 700)),
+                   D=int(rng.choice([16, 32, 64, 80, 96, 128])), causal=bool(rng.integers(0, 2)),
+                   seed=int(rng.integers(0, 1 << 30)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", list(_random_cases(1700, 10)), ids=lambda c: "B{B}H{H}S{S}D{D}c{causal:d}".format(**c))
+def test_random_shapes(case, dtype):
+    """Seeded random shapes (ragged S, every head dim, causal or not) through the whole path."""
+    c = case
+    q, k, v, do = make_inputs(c["B"], c["H"], c["S"], c["D"], dtype, seed=c["seed"])
+    check_full(q, k, v, do, dtype, causal=c["causal"], label=f"random {c}")
+
+
+@pytest.mark.parametrize("case", list(range(8)))
+def test_random_key_sets(case):
+    """Seeded random query/key shard sizes and offsets through the key-set forward and backward:
+    the shifted forward against the oracle, and the backward contributions against the oracle's
+    with the same L and Delta."""
+    rng = np.random.default_rng(1800 + case)
+    dev = torch.device("cuda:0")
+    Sq, Sk = int(rng.integers(1, 400)), int(rng.integers(1, 400))
+    off = int(rng.integers(-Sq - 20, Sk + 20))
+    D = int(rng.choice([16, 64, 80, 128]))
+    dtype = "bf16" if case % 2 == 0 else "f32"
+    causal = bool(rng.integers(0, 4))          # mostly causal
+    q, _, _, do = make_inputs(1, 2, Sq, D, dtype, seed=1900 + case)
+    _, k, v, _ = make_inputs(1, 2, Sk, D, dtype, seed=2000 + case)
+    qn, kn, vn, don = (x.double().numpy() for x in (q, k, v, do))
+    label = f"key set Sq={Sq} Sk={Sk} off={off} D={D} {dtype} causal={causal}"
+    print(f"[parity] {label}", flush=True)
+    op, lp = fa.forward_partial(q.to(dev), k.to(dev), v.to(dev), causal=causal, q_offset=off)
+    torch.cuda.synchronize()
+    r_o, r_l = oracle.forward_offset(qn, kn, vn, q_offset=off, causal=causal)
+    _check_partial(op[0].double().cpu().numpy(), lp[0].double().cpu().numpy(), r_o, r_l, dtype, label)
+    delta = np.einsum("bhsd,bhsd->bhs", r_o, don)
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).float().to(dev)
+    g = fa.backward_partial(q.to(dev), k.to(dev), v.to(dev), do.to(dev), f32(r_l), f32(delta),
+                            causal=causal, q_offset=off)
+    torch.cuda.synchronize()
+    r = oracle.backward_partial(qn, kn, vn, don, r_l, delta, q_offset=off, causal=causal)
+    for name, g_, r_ in zip(("dq", "dk", "dv"), g, r):
+        g_ = g_.double().cpu().numpy()
+        if np.max(np.abs(r_)) <= 1e-9:
+            # nothing contributes (no allowed pair) or cancellation (a single key)
+            assert np.max(np.abs(g_)) <= 1e-4, (label, name)
+            continue
+        e = rel(g_, r_)
+        assert e <= TOL[dtype]["grad"], (label, name, e)
+
+
 def test_custom_scale_and_peaky_scores():
     q, k, v, do = make_inputs(1, 2, 257, 64, "bf16", seed=7, qk_mult=3.0)
     check_full(q, k, v, do, "bf16", causal=True, scale=0.3, label="scale=0.3 peaky")
