@@ -17,7 +17,9 @@
  * contiguous row-major block [B][H][S][D] of `dtype` elements in device
  * memory (heads folded into the batch, as in the handout's launch grid
  * (T_q, batch)); lse and delta are contiguous [B][H][S] fp32.  Queries and
- * keys share the length S and both start at position 0.
+ * keys share the length S and both start at position 0, except in the
+ * key-set calls (fa_fwd_partial, fa_bwd_partial), which take the two lengths
+ * and the queries' offset from key 0 separately.
  *
  * Ownership.  The caller allocates every buffer (including the backward
  * workspace); the library never allocates, frees,
