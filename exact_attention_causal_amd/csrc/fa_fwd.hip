@@ -22,8 +22,10 @@
 //   * K and V tiles sit row-major in LDS with a padded pitch; V^T operand
 //     fragments come straight from the row-major tile through the gfx950
 //     transposing LDS read, so nothing is transposed on the way in;
-//   * the accumulator is rescaled only when a new score exceeds the running
-//     maximum by 2^8 (exactness is kept because O and l share the stale max);
+//   * the running maximum is allowed to lag: a tile is exponentiated against
+//     it as it stands and kept when the probabilities stay below 2^8, so most
+//     tiles form no row maximum and rescale nothing (exactness is kept because
+//     O and l share the stale max);
 //   * K/V tiles are loaded straight into LDS (global_load_lds_dwordx4) into
 //     three stages, so the next two tiles stream in while the current one is
 //     used and no registers or VALU work are spent staging them;
@@ -49,10 +51,14 @@ struct FwdTile {
     static_assert(D % 16 == 0 && BK % 32 == 0 && NW % 2 == 0, "tile shape");
 };
 
-// Scores more than 2^kRescaleSlack above the running maximum force a rescale;
-// below that, p = exp2(s - m) stays <= 2^kRescaleSlack, which fp32 and bf16
-// hold exactly as well as values <= 1, and O and l keep the same stale m.
+// The running maximum m may lag the scores: a tile whose probabilities
+// p = exp2(s - m) sum to at most 2^kRescaleSlack per lane (16 or 32 of them)
+// is accepted as it is -- such p are held by fp32 and bf16 exactly as well as
+// values <= 1, and O and l share the stale m -- and only a larger sum makes
+// the tile take the exact path, which moves m to the tile's maximum.
 constexpr float kRescaleSlack = 8.f;
+constexpr float kRescaleSum = 256.f;  // 2^kRescaleSlack
+static_assert(kRescaleSum == (float)(1 << (int)kRescaleSlack), "sum limit");
 
 // Problem shape of one launch.  Query i of a head sits `off` positions after
 // key 0, so the causal mask allows key j iff j <= i + off (off = 0 and
@@ -194,8 +200,8 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
                 group(std::integral_constant<int, C::NSD % KG>{}, C::NSD / KG * KG);
         }
     };
-    // mask, online softmax and row sums of tile j's scores (P left in s)
-    auto softmax = [&](int j) {
+    // scores of tile j that a query may not see become -inf
+    auto mask = [&](int j) {
         const int j0 = j * BK;
         const bool need_mask = (causal && j0 + BK - 1 > qw0 + off) || (j0 + BK > Sk);
         if (need_mask) {
@@ -215,40 +221,68 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
                         s[qb][kb][r] = (32 * kb + ridx(r, 0) < t) ? s[qb][kb][r] : -INFINITY;
             }
         }
-        // Online softmax in base 2 (scores scaled by c = scale*log2 e).  The
-        // running maximum only moves when a score exceeds it by kRescaleSlack.
+    };
+    // Online softmax of tile j in base 2 (scores scaled by c = scale*log2 e),
+    // P left in s and its row sums added to l.  Fast path: exponentiate against
+    // the running maxima as they stand, and keep the result when every lane's
+    // sum (so every p) is at most 2^kRescaleSlack: no row maximum is formed.
+    // Otherwise the tile's scores are formed again and the exact path moves
+    // each row's maximum to the tile's own.  A row that has seen no key yet
+    // (m = -inf) always takes the exact path: its fast sum is inf or NaN.
+    auto softmax = [&](const T *tK, int j) {
+        mask(j);
+        float ps[NQB];
+        bool ok = true;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-            mx = wave_xor32_max(mx) * c;
-            const bool grow = mx > mrow[qb] + kRescaleSlack;
-            if (__ballot(grow) != 0) {  // wave-uniform: rare after the first tile
-                const float mnew = grow ? mx : mrow[qb];
-                // (a row that has seen no key yet keeps -inf: its alpha is 1,
-                // not exp2(-inf - -inf))
-                const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mrow[qb] - mnew);
-                lrow[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
-                mrow[qb] = mnew;
-            }
-            // a row whose maximum is still -inf has seen only masked keys: use 0
-            const float muse = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
-            float ps = 0.f;
+            ps[qb] = 0.f;
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(fmaf(s[qb][kb][r], c, -muse));
+                    const float p = fast_exp2(fmaf(s[qb][kb][r], c, -mrow[qb]));
                     s[qb][kb][r] = p;
-                    ps += p;
+                    ps[qb] += p;
                 }
-            lrow[qb] += ps;
+            ok = ok && ps[qb] <= kRescaleSum;  // (false for inf and NaN)
         }
+        if (__ballot(!ok) != 0) {  // wave-uniform: rare after a row's first tile
+            qk(tK, -1);
+            mask(j);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+                mx = wave_xor32_max(mx) * c;
+                const bool grow = mx > mrow[qb];
+                if (__ballot(grow) != 0) {
+                    const float mnew = grow ? mx : mrow[qb];
+                    // (a row that has seen no key yet keeps -inf: its alpha is
+                    // 1, not exp2(-inf - -inf))
+                    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mrow[qb] - mnew);
+                    lrow[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
+                    mrow[qb] = mnew;
+                }
+                // a row whose maximum is still -inf has seen only masked keys: use 0
+                const float muse = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
+                ps[qb] = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float p = fast_exp2(fmaf(s[qb][kb][r], c, -muse));
+                        s[qb][kb][r] = p;
+                        ps[qb] += p;
+                    }
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) lrow[qb] += ps[qb];
     };
     // O^T += V^T P^T; prefetch part p0 + kb goes out before key block kb (p0 < 0: none)
     auto pv = [&](const T *tV, int p0) {
@@ -285,7 +319,7 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
             all_parts();
         } else {
             qk(tK, 0);
-            softmax(j);
+            softmax(tK, j);
             pv(tV, C::NKB);
         }
         wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
