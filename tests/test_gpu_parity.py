@@ -554,6 +554,75 @@ def test_custom_scale_and_peaky_scores():
     check_full(q, k, v, do, "bf16", causal=True, scale=0.3, label="scale=0.3 peaky")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("slope,jump", [(0.065, 0.0), (0.4, 0.0), (0.0, 150.0), (0.02, 90.0)])
+def test_rising_scores(slope, jump, dtype):
+    """Scores that rise along the keys, so the running row maximum has to move
+    tile after tile.
+
+    Key j scores about slope*j (natural-log units), plus `jump` from the middle
+    key on.  slope 0.065 lifts each 64-key tile by about 4 (6 in base 2): its
+    probabilities against the maximum so far sum past 2^8 while each stays
+    below it.  slope 0.4 lifts each tile by about 25.  Jumps of 90 and 150
+    make the exponentials against the maximum before them overflow to inf.
+    """
+    B, H, S, D = 1, 2, 777, 64
+    g = torch.Generator("cpu").manual_seed(31)
+    u = torch.randn(D, generator=g)
+    u = u / u.norm()
+    pos = torch.arange(S, dtype=torch.float32)
+    a = slope * pos + jump * (pos >= S // 2).float()
+    # scale 1/8 and q . k_j = 8 a_j: the score of key j is about a_j.  The keys
+    # also get a part orthogonal to the queries' direction, as large as a_j:
+    # without it the keys a row attends to share one large component, and
+    # dQ = scale * sum_j dS_ij k_j (whose dS sum to zero over j) would be a
+    # near-total cancellation that no bf16 path computes to 5e-2.
+    q = 8.0 * u + 0.05 * torch.randn(B, H, S, D, generator=g)
+    w = torch.randn(B, H, S, D, generator=g)
+    w = w - (w @ u)[..., None] * u
+    k = a[:, None] * u + (0.5 * a + 1.0)[:, None] * w
+    v, do = (torch.randn(B, H, S, D, generator=g) for _ in range(2))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v, do = (x.to(tdt) for x in (q, k, v, do))
+    check_full(q, k, v, do, dtype, causal=True, label=f"rising slope={slope} jump={jump}")
+    check_full(q, k, v, do, dtype, causal=False, label=f"rising slope={slope} jump={jump} non-causal")
+    if dtype == "bf16":
+        # the shifted-key forward over three key chunks, merged
+        dev = torch.device("cuda:0")
+        o, lse = fa.forward_split_kv(q.to(dev), k.to(dev), v.to(dev), 3)
+        torch.cuda.synchronize()
+        r_o, r_l = oracle.forward(*(x.double().numpy() for x in (q, k, v)), causal=True)
+        assert rel(o.double().cpu().numpy(), r_o) <= TOL["bf16"]["o"]
+        assert absdiff(lse.double().cpu().numpy(), r_l) <= TOL["bf16"]["lse"]
+
+
+def test_rising_scores_wide_tile():
+    """The same on the 64-queries-per-wave forward tile (bf16, D = 128, enough
+    query tiles to select it): scores rise by about 4.8 per 32-key tile over
+    the first 1024 keys (7 in base 2: the tile's sums pass 2^8, each
+    probability stays below it), then jump by 100 at key 3000 (overflow)."""
+    B, H, S, D = 1, 128, 4096, 128
+    g = torch.Generator("cpu").manual_seed(41)
+    u = torch.randn(D, generator=g)
+    u = u / u.norm()
+    pos = torch.arange(S, dtype=torch.float32)
+    a = 0.152 * torch.clamp(pos, max=1024.0) + 100.0 * (pos >= 3000).float()
+    # default scale 1/sqrt(D) and q . k_j = sqrt(D) a_j: the score of key j is about a_j
+    q = D ** 0.5 * u + 0.05 * torch.randn(B, H, S, D, generator=g)
+    k = a[:, None] * u + 0.05 * torch.randn(B, H, S, D, generator=g)
+    v = torch.randn(B, H, S, D, generator=g)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    dev = torch.device("cuda:0")
+    print("[parity] rising scores, wide forward tile", flush=True)
+    o, lse = fa.forward(q.to(dev), k.to(dev), v.to(dev), causal=True)
+    torch.cuda.synchronize()
+    for hh in (0, 77):
+        r_o, r_l = oracle.forward(*(x[:, hh:hh + 1].double().numpy() for x in (q, k, v)),
+                                  causal=True)
+        assert rel(o[:, hh:hh + 1].double().cpu().numpy(), r_o) <= TOL["bf16"]["o"], hh
+        assert absdiff(lse[:, hh:hh + 1].double().cpu().numpy(), r_l) <= TOL["bf16"]["lse"], hh
+
+
 def test_first_query_and_identical_keys():
     """Closed forms on the GPU: O_0 = V_0; identical keys give the causal prefix mean."""
     S, D = 300, 64
