@@ -292,6 +292,82 @@ struct TransReader {
     }
 };
 
+// ---- 16-row output tails (bf16, D = 16 (mod 32)) --------------------------
+//
+// A head dimension of 32k + 16 leaves a last output block of 16 rows.  It is
+// formed with v_mfma_f32_16x16x32_bf16 (half the matrix-core time of a padded
+// 32x32x16 pair) as two 16-column blocks, one per 16 columns of the 32x32
+// block whose B operand it shares:
+//   * output (16 x 16): lane 16g + i, register r holds C[row 4g + r][col i];
+//   * B operand (32 x 16): lane 16g + i holds 8 k-slots for column i.  From
+//     the two B fragments of a 32x32 output block (registers 0..7 and 8..15,
+//     i.e. reduction rows 16u + 2h + {0,4,8,12,1,5,9,13}), one half-row swap
+//     (v_permlane16_swap: odd 16-lane rows of the first with even rows of the
+//     second) leaves in the first fragment the operand of columns 0..15 and in
+//     the second that of columns 16..31, with lane group g holding reduction
+//     rows b_g + {0,4,8,12,1,5,9,13}, b_g = 16*(g&1) + 2*(g>>1);
+//   * A operand (16 x 32): lane 16g + i holds row i at those reduction rows,
+//     which two transposing LDS reads deliver (TailReader).
+__device__ inline f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// B operands of the two 16-column tail blocks from the two B fragments of a
+// 32x32 output block (see above).
+__device__ inline void tail_bfrag(const bf16x8 (&pf)[2], bf16x8 &b0, bf16x8 &b1) {
+    u32x4 x = __builtin_bit_cast(u32x4, pf[0]), y = __builtin_bit_cast(u32x4, pf[1]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x[w], y[w], false, false);
+        x[w] = r[0];
+        y[w] = r[1];
+    }
+    b0 = __builtin_bit_cast(bf16x8, x);
+    b1 = __builtin_bit_cast(bf16x8, y);
+}
+
+// A value held per 32x32 column (lane l and l ^ 32 hold column l % 32), as the
+// two tail blocks need it: lane 16g + i gets column i (first) and 16 + i (second).
+__device__ inline void tail_cols(float x, float &c0, float &c1) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    c0 = __uint_as_float(r[0]);
+    c1 = __uint_as_float(r[1]);
+}
+
+// A operand of a 16-row tail: rows are columns c0..c0+15 of a padded tile,
+// reducing over tile rows 32*kb + b_g + {0,4,8,12,1,5,9,13}.  In each 16-lane
+// group the transposing read gives lane i column i of the four rows that
+// lanes 4e..4e+3 point at (row b_g + 4e, columns 4c..4c+3 for lane 4e + c).
+template <int D>
+struct TailReader {
+    using PD = Pad<bf16, D>;
+    int base;
+    __device__ inline void init(int lane) {
+        const int g = lane >> 4, j = lane & 15, e = j >> 2, c = j & 3;
+        base = (16 * (g & 1) + 2 * (g >> 1) + 4 * e) * PD::PITCH + 4 * c;
+    }
+    __device__ inline bf16x8 load(const bf16 *tile, int kb, int c0) const {
+        typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+        const bf16 *p = tile + base + 32 * kb * PD::PITCH + c0;
+        const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+        const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + PD::PITCH));
+        return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+};
+
+// Store 4 consecutive output elements (fp32 values * mul, rounded to T).
+template <typename T>
+__device__ inline void store4(T *dst, const f32x4 &c, float mul) {
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (bf16)(c[t] * mul);
+        *reinterpret_cast<bf16x4 *>(dst) = v;
+    } else {
+        *reinterpret_cast<f32x4 *>(dst) = f32x4{c[0] * mul, c[1] * mul, c[2] * mul, c[3] * mul};
+    }
+}
+
 // Store 8 consecutive output elements (fp32 values * mul, rounded to T).
 template <typename T>
 __device__ inline void store8(T *dst, const f32x16 &c, int r0, float mul) {

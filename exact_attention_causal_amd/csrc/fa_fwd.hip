@@ -44,7 +44,9 @@ struct FwdTile {
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;           // MFMAs over d per 32x32 block
     static constexpr int NKB = BK / 32;               // 32-key blocks per tile
-    static constexpr int ND = (D + 31) / 32;          // 32-row output blocks over d
+    // bf16 D = 16 (mod 32): the last 16 output rows form a 16-row tail
+    static constexpr bool TAIL = KPL == 8 && D % 32 == 16;
+    static constexpr int ND = TAIL ? D / 32 : (D + 31) / 32;  // 32-row output blocks over d
     static constexpr int NI = 16 / KPL;               // MFMAs per 32-key reduction block
     using DMA = TileDma<T, D, BK, NW / 2>;           // half the waves load K, half V
     static constexpr int TILE = DMA::ELEMS;           // elements per K or V tile
@@ -125,8 +127,11 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
     }
     TransReader<T, D> vt;
     vt.init(lane);
+    TailReader<D> tt;  // (16-row tail only)
+    if constexpr (C::TAIL) tt.init(lane);
 
-    f32x16 acc[NQB][C::ND];
+    f32x16 acc[NQB][C::ND > 0 ? C::ND : 1];
+    f32x4 tacc[NQB][2];  // 16-row tail: queries 0..15 and 16..31 of the block
     float mrow[NQB], lrow[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -134,6 +139,8 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
         lrow[qb] = 0.f;
 #pragma unroll
         for (int db = 0; db < C::ND; ++db) acc[qb][db] = f32x16{};
+        tacc[qb][0] = f32x4{};
+        tacc[qb][1] = f32x4{};
     }
 
     const int qend = min(q0 + C::BQ, S);
@@ -266,6 +273,12 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
                     lrow[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < C::ND; ++db) acc[qb][db] *= alpha;
+                    if constexpr (C::TAIL) {
+                        float a0, a1;
+                        tail_cols(alpha, a0, a1);
+                        tacc[qb][0] *= a0;
+                        tacc[qb][1] *= a1;
+                    }
                     mrow[qb] = mnew;
                 }
                 // a row whose maximum is still -inf has seen only masked keys: use 0
@@ -300,6 +313,16 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
                 for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(vf[i], pf[qb][i], acc[qb][db]);
+            }
+            if constexpr (C::TAIL) {
+                const bf16x8 ta = tt.load(tV, kb, 32 * C::ND);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    bf16x8 b0, b1;
+                    tail_bfrag(pf[qb], b0, b1);
+                    tacc[qb][0] = mma16(ta, b0, tacc[qb][0]);
+                    tacc[qb][1] = mma16(ta, b1, tacc[qb][1]);
+                }
             }
         }
     };
@@ -336,11 +359,22 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
     for (int qb = 0; qb < NQB; ++qb) {
         const int qi = qw0 + qb * 32 + l32;
         const float lt = wave_xor32_sum(lrow[qb]);
+        // a row that allows no key of this launch (shifted or split keys
+        // only) has the empty result O = 0, L = -inf
+        const bool empty = !(lt > 0.f);
+        const float inv = empty ? 0.f : 1.f / lt;
+        if constexpr (C::TAIL) {
+            // tail lane 16g + i holds rows 4g..4g+3 of queries i and 16 + i
+            float i0, i1;
+            tail_cols(inv, i0, i1);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int qt_ = qw0 + qb * 32 + 16 * t + (lane & 15);
+                if (qt_ < S)
+                    store4<OutT>(o + (size_t)qt_ * D + 32 * C::ND + 4 * (lane >> 4), tacc[qb][t], t ? i1 : i0);
+            }
+        }
         if (qi < S) {
-            // a row that allows no key of this launch (shifted or split keys
-            // only) has the empty result O = 0, L = -inf
-            const bool empty = !(lt > 0.f);
-            const float inv = empty ? 0.f : 1.f / lt;
 #pragma unroll
             for (int db = 0; db < C::ND; ++db)
 #pragma unroll
