@@ -127,6 +127,21 @@ __device__ inline void out8(OutT *dst, const f32x16 &acc, int r0, float mul, int
         store8<OutT>(dst, acc, r0, mul);
     }
 }
+// The same for the 4 consecutive elements a lane holds of a 16-row tail block.
+template <bool GEN, typename OutT>
+__device__ inline void out4(OutT *dst, const f32x4 &acc, float mul, int accumulate) {
+    if constexpr (GEN) {
+        if (accumulate) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(dst);
+            store4<OutT>(dst, f32x4{fmaf(acc[0], mul, a[0]), fmaf(acc[1], mul, a[1]),
+                                    fmaf(acc[2], mul, a[2]), fmaf(acc[3], mul, a[3])}, 1.f);
+        } else {
+            store4<OutT>(dst, acc, mul);
+        }
+    } else {
+        store4<OutT>(dst, acc, mul);
+    }
+}
 
 template <typename T, int D_, int BQ2_>
 struct KvTile {
@@ -425,7 +440,9 @@ struct KvTile1 {
     static constexpr int BKV = NW * 32;               // keys per workgroup
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;
-    static constexpr int ND = (D + 31) / 32;
+    // bf16 D = 16 (mod 32): the last 16 rows of dV^T, dK^T form a 16-row tail
+    static constexpr bool TAIL = KPL == 8 && D % 32 == 16;
+    static constexpr int ND = TAIL ? D / 32 : (D + 31) / 32;
     static constexpr int NI = 16 / KPL;
     using DMA = TileDma<T, D, BQ, NW / 2>;           // half the waves load Q, half dO
     // a Q (dO) tile array also carries the tile's L (D) values: 64 slots per
@@ -500,8 +517,11 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     }
     TransReader<T, D> tr;
     tr.init(lane);
+    TailReader<D> tt;  // (16-row tail only)
+    if constexpr (C::TAIL) tt.init(lane);
 
-    f32x16 accV[C::ND], accK[C::ND];  // dV^T and -dK^T
+    f32x16 accV[C::ND > 0 ? C::ND : 1], accK[C::ND > 0 ? C::ND : 1];  // dV^T and -dK^T
+    f32x4 tailV[2] = {f32x4{}, f32x4{}}, tailK[2] = {f32x4{}, f32x4{}};  // 16-row tails: keys 0..15, 16..31
 #pragma unroll
     for (int db = 0; db < C::ND; ++db) {
         accV[db] = f32x16{};
@@ -600,6 +620,13 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) accV[db] = M::run(at[i], pf[i], accV[db]);
                 }
+                if constexpr (C::TAIL) {
+                    bf16x8 b0, b1;
+                    tail_bfrag(pf, b0, b1);
+                    const bf16x8 ta = tt.load(tdO, qb, 32 * C::ND);
+                    tailV[0] = mma16(ta, b0, tailV[0]);
+                    tailV[1] = mma16(ta, b1, tailV[1]);
+                }
             }
             // D - dP (Eq. 16), then -dS = P o (D - dP) (Eq. 17)
             f32x16 dp;
@@ -633,6 +660,13 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
 #pragma unroll
                     for (int i = 0; i < C::NI; ++i) accK[db] = M::run(at[i], sf[i], accK[db]);
                 }
+                if constexpr (C::TAIL) {
+                    bf16x8 b0, b1;
+                    tail_bfrag(sf, b0, b1);
+                    const bf16x8 ta = tt.load(tQ, qb, 32 * C::ND);
+                    tailK[0] = mma16(ta, b0, tailK[0]);
+                    tailK[1] = mma16(ta, b1, tailK[1]);
+                }
             }
         };
 #pragma unroll
@@ -665,6 +699,18 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
                 }
             }
     }
+    if constexpr (C::TAIL) {
+        // tail lane 16g + i holds rows 4g..4g+3 of the wave's keys i and 16 + i
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int kt_ = kw0 + 16 * t + (lane & 15);
+            const int d0 = 32 * C::ND + 4 * (lane >> 4);
+            if (kt_ < Sk) {
+                out4<GEN>(dv + (size_t)kt_ * D + d0, tailV[t], 1.f, a.accumulate);
+                out4<GEN>(dk + (size_t)kt_ * D + d0, tailK[t], -a.scale, a.accumulate);
+            }
+        }
+    }
 }
 
 // -------------------------------------------------------- query-outer dQ ---
@@ -677,7 +723,9 @@ struct QTile {
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;
     static constexpr int NKB = BK / 32;
-    static constexpr int ND = (D + 31) / 32;
+    // bf16 D = 16 (mod 32): the last 16 rows of dQ^T form a 16-row tail
+    static constexpr bool TAIL = KPL == 8 && D % 32 == 16;
+    static constexpr int ND = TAIL ? D / 32 : (D + 31) / 32;
     static constexpr int NI = 16 / KPL;
     using DMA = TileDma<T, D, BK, NW / 2>;           // half the waves load K, half V
     static constexpr int TILE = DMA::ELEMS;           // elements per K or V tile
@@ -744,12 +792,18 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     for (int qb = 0; qb < NQB; ++qb) neg_run<T, C::NSD>(df[qb]);
     TransReader<T, D> tr;
     tr.init(lane);
+    TailReader<D> tt;  // (16-row tail only)
+    if constexpr (C::TAIL) tt.init(lane);
 
-    f32x16 acc[NQB][C::ND];
+    f32x16 acc[NQB][C::ND > 0 ? C::ND : 1];
+    f32x4 tacc[NQB][2];  // 16-row tail: queries 0..15 and 16..31 of the block
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+    for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
         for (int db = 0; db < C::ND; ++db) acc[qb][db] = f32x16{};
+        tacc[qb][0] = f32x4{};
+        tacc[qb][1] = f32x4{};
+    }
 
     const int qend = min(q0 + C::BQ, S);
     int nkt = (Sk + BK - 1) / BK;
@@ -823,6 +877,13 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 #pragma unroll
                         for (int i = 0; i < C::NI; ++i) acc[qb][db] = M::run(a[i], sf[i], acc[qb][db]);  // Eq. 18
                     }
+                    if constexpr (C::TAIL) {
+                        bf16x8 b0, b1;
+                        tail_bfrag(sf, b0, b1);
+                        const bf16x8 ta = tt.load(tK, kb, 32 * C::ND);
+                        tacc[qb][0] = mma16(ta, b0, tacc[qb][0]);
+                        tacc[qb][1] = mma16(ta, b1, tacc[qb][1]);
+                    }
                 }
             }
         }
@@ -846,6 +907,16 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
                     const int d0 = db * 32 + 16 * hr + 8 * h;
                     if (d0 < D) out8<GEN>(dq + (size_t)qi * D + d0, acc[qb][db], 8 * hr, -a.scale, a.accumulate);
                 }
+        }
+        if constexpr (C::TAIL) {
+            // tail lane 16g + i holds rows 4g..4g+3 of queries i and 16 + i of the block
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int qt_ = qw0 + qb * 32 + 16 * t + (lane & 15);
+                if (qt_ < S)
+                    out4<GEN>(dq + (size_t)qt_ * D + 32 * C::ND + 4 * (lane >> 4), tacc[qb][t], -a.scale,
+                              a.accumulate);
+            }
         }
     }
 }
