@@ -38,7 +38,7 @@ DEFAULT_WORKLOAD = "bf16_b1h16_s65536_d128"
 # rocprofv3 --pmc passes (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a
 # plain 1 GiB copy calibrates; see profiles/), keyed by a hash of the forward
 # kernel's sources: once those change, the figure is stale and reported as null.
-FWD_TRAFFIC = {"sources_sha1": "c050bbe80e86203f2891c7e3444862409b9d1921", "bytes": 9504706080}
+FWD_TRAFFIC = {"sources_sha1": "1ea89c8c08409000bb7b832e54c6d27e66b78899", "bytes": 9504343360}
 FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp")
 
 
