@@ -427,19 +427,24 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
 // price is both K^T and V^T and both accumulators in registers, which the
 // narrower head dimensions afford at two waves per SIMD.
 
-template <typename T, int D_, int NW_, bool VLDS_ = false, int NQB_ = 1, int NSTAGE_ = 3>
+template <typename T, int D_, int NW_, bool VLDS_ = false, int NQB_ = 1, int NSTAGE_ = 3, int VREG_ = 0>
 struct KvTile1 {
     static constexpr int D = D_, NW = NW_, NT = NW * kWave;
     static constexpr int NQB = NQB_;                  // 32-query blocks per step
     // LDS stages of Q/dO tiles: 3 (two tiles in flight) or 2 (one)
     static constexpr int NSTAGE = NSTAGE_;
-    // -V^T read from LDS every step (written there once) instead of held in
-    // registers: 4 * D / (16 / KPL) fewer registers per lane
+    // -V^T partly in LDS (written there once, read every step): the first
+    // VREG fragments of a lane's run stay in registers, the other VL in LDS
+    // (4 * KPL * VL / 8 fewer registers per lane, VL reads per block)
     static constexpr bool VLDS = VLDS_;
     static constexpr int BQ = 32 * NQB;               // queries per step
     static constexpr int BKV = NW * 32;               // keys per workgroup
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;
+    static constexpr int VREG = VREG_, VL = NSD - VREG_;
+    // LDS row of a key's -V^T part: both lane halves' VL fragments plus a
+    // 16-byte pad (4 (mod 8) words, conflict-free like every tile)
+    static constexpr int VPITCH = 2 * VL * KPL + 16 / (int)sizeof(T);
     // bf16 D = 16 (mod 32): the last 16 rows of dV^T, dK^T form a 16-row tail
     static constexpr bool TAIL = KPL == 8 && D % 32 == 16;
     static constexpr int ND = TAIL ? D / 32 : (D + 31) / 32;
@@ -450,6 +455,7 @@ struct KvTile1 {
     static constexpr int XOFF = DMA::ELEMS;
     static constexpr int TILE = DMA::ELEMS + (NW / 2) * kWave * 4 / (int)sizeof(T);
     static_assert(D % 16 == 0 && NW % 2 == 0 && (NQB == 1 || NQB == 2), "tile shape");
+    static_assert(VREG >= 0 && VREG < NSD && (VLDS || VREG == 0), "-V^T split");
     static_assert(NSTAGE == 2 || NSTAGE == 3, "stages");
 };
 
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE], sQ2[T3];
     __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE], sdO2[T3];
     using PD = typename C::DMA::PD;
-    __shared__ __attribute__((aligned(16))) T sV[C::VLDS ? C::BKV * PD::PITCH : 8];
+    __shared__ __attribute__((aligned(16))) T sV[C::VLDS ? C::BKV * C::VPITCH : 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -492,9 +498,9 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     const int key = kw0 + l32;  // this lane's key column
 
     // B operands: K^T and -V^T (the dP chain then yields D - dP)
-    frag bk[C::NSD], bv[C::VLDS ? 1 : C::NSD];
+    frag bk[C::NSD], bv[C::VLDS ? (C::VREG > 0 ? C::VREG : 1) : C::NSD];
     // this lane's -V^T run in LDS (its own row: no other wave reads it)
-    T *const sVl = sV + (C::VLDS ? (wave * 32 + l32) * PD::PITCH + h * (D / 2) : 0);
+    T *const sVl = sV + (C::VLDS ? (wave * 32 + l32) * C::VPITCH + h * C::VL * C::KPL : 0);
     if (key < Sk) {
         load_run<T, C::NSD>(bk, k + (size_t)key * D + h * (D / 2));
     } else {
@@ -509,7 +515,10 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
         neg_run<T, C::NSD>(vt0);
         if constexpr (C::VLDS) {
 #pragma unroll
-            for (int i = 0; i < C::NSD; ++i) *reinterpret_cast<frag *>(sVl + i * C::KPL) = vt0[i];
+            for (int i = 0; i < C::NSD; ++i) {
+                if (i < C::VREG) bv[i < C::VREG ? i : 0] = vt0[i];  // (index kept in range for the compiler)
+                else *reinterpret_cast<frag *>(sVl + (i - C::VREG) * C::KPL) = vt0[i];
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < C::NSD; ++i) bv[i] = vt0[i];
@@ -638,10 +647,11 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
                 frag da[C::NSD];
                 load_row_frags<T, D>(da, tdO, 32 * qb + rsigma(l32), h);
                 if constexpr (C::VLDS) {
-                    frag bvl[C::NSD];
-                    load_run<T, C::NSD>(bvl, sVl);
+                    frag bvl[C::VL];
+                    load_run<T, C::VL>(bvl, sVl);
 #pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bvl[st], dp);
+                    for (int st = 0; st < C::NSD; ++st)
+                        dp = M::run(da[st], st < C::VREG ? bv[st < C::VREG ? st : 0] : bvl[st < C::VREG ? 0 : st - C::VREG], dp);
                 } else {
 #pragma unroll
                     for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bv[st], dp);
@@ -939,13 +949,15 @@ template <typename T, int D>
 using KvTileFor = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
 template <typename T, int D>
 using QTileFor = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
-// (bf16 D = 128 keeps -V^T in LDS: with it in registers the kernel spills.
-// Two 32-query blocks per step halve the barriers and DMA issues per
-// product: 4-5 % faster up to D = 96; at D = 128 the LDS holds them beside
-// -V^T only with two stages (1 % faster than one block with three).)
+// (bf16 D = 128 keeps half of -V^T in LDS: with all of it in registers the
+// kernel spills; half in registers (254 VGPRs) reads half as much LDS per
+// block: the backward ran 1.3 % faster than with all of it in LDS.  Two 32-query blocks per
+// step halve the barriers and DMA issues per product: 4-5 % faster up to
+// D = 96; at D = 128 the LDS holds them beside -V^T only with two stages
+// (1 % faster than one block with three).)
 template <typename T, int D>
 using KvTile1For = KvTile1<T, D, 8, sizeof(T) == 2 && D == 128, sizeof(T) == 2 ? 2 : 1,
-                           (sizeof(T) == 2 && D == 128) ? 2 : 3>;
+                           (sizeof(T) == 2 && D == 128) ? 2 : 3, (sizeof(T) == 2 && D == 128) ? 4 : 0>;
 // dK/dV with one wave per key block for bf16 (faster than pairs by 6 % at
 // D = 80, 10 % at D = 64 and 5 % at D = 128); pairs of waves for fp32, whose
 // wider fragments do not fit two waves per SIMD with both operands held
