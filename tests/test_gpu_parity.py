@@ -291,7 +291,7 @@ def _check_partial(g_o, g_l, r_o, r_l, dtype, label):
     (64, 200, -64, 1),     # no query sees any key
     (90, 130, 0, 0),       # no mask
 ])
-@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 80)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 80), ("bf16", 80)])
 def test_fwd_partial_shifted(Sq, Sk, off, causal, dtype, D):
     dev = torch.device("cuda:0")
     q, _, _, _ = make_inputs(2, 2, Sq, D, dtype, seed=600 + Sq)
@@ -383,7 +383,7 @@ def _stats_over(q, k, v, do, off, causal):
     (90, 230, 0, 0),       # no mask
     (1, 1, 0, 1),          # one query, one key
 ])
-@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 80), ("bf16", 16)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 80), ("bf16", 16), ("bf16", 80)])
 def test_bwd_partial_shifted(Sq, Sk, off, causal, dtype, D):
     dev = torch.device("cuda:0")
     q, _, _, do = make_inputs(2, 2, Sq, D, dtype, seed=1100 + Sq)
@@ -413,10 +413,12 @@ def test_bwd_partial_shifted(Sq, Sk, off, causal, dtype, D):
         assert e <= TOL[dtype]["grad"], (label, name, e)
 
 
-def test_bwd_partial_accumulates():
+@pytest.mark.parametrize("D", [64, 80])
+def test_bwd_partial_accumulates(D):
     # accumulate = 1 adds the contributions to what the buffers hold; 0 overwrites
+    # (D = 80 also covers the 16-row output tails)
     dev = torch.device("cuda:0")
-    Sq, Sk, off, D = 150, 333, 120, 64
+    Sq, Sk, off = 150, 333, 120
     q, _, _, do = make_inputs(1, 3, Sq, D, "bf16", seed=1300)
     _, k, v, _ = make_inputs(1, 3, Sk, D, "bf16", seed=1301)
     qn, kn, vn, don = (x.double().numpy() for x in (q, k, v, do))
