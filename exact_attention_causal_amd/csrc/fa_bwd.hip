@@ -472,7 +472,6 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     constexpr int T3 = C::NSTAGE == 3 ? C::TILE : 8;
     __shared__ __attribute__((aligned(1024))) T sQ0[C::TILE], sQ1[C::TILE], sQ2[T3];
     __shared__ __attribute__((aligned(1024))) T sdO0[C::TILE], sdO1[C::TILE], sdO2[T3];
-    using PD = typename C::DMA::PD;
     __shared__ __attribute__((aligned(16))) T sV[C::VLDS ? C::BKV * C::VPITCH : 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
