@@ -61,11 +61,20 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int 
     return map_launch(fa::launch_delta(dtype, o, dout, delta, B * H, S, D, stream));
 }
 
+// The part of the backward workspace every call needs: the base-2 copy of
+// lse, one fp32 per row, rounded up to 256 bytes.
+static size_t bwd_base_workspace(int B, int H, int S) {
+    return ((size_t)B * H * S * sizeof(float) + 255) & ~(size_t)255;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype) {
     if (check_shape(B, H, S, D, dtype) != FA_OK) return 0;
-    // base-2 copy of lse: one fp32 per row
-    const size_t bytes = (size_t)B * H * S * sizeof(float);
-    return (bytes + 255) & ~(size_t)255;
+    const size_t bytes = bwd_base_workspace(B, H, S);
+    // bf16 problems with few key tiles per CU: fp32 partial dQ, dK, dV of
+    // each chunk of the split backward
+    const fa::BwdSplit sp = fa::bwd_split(dtype, B * H, S, D);
+    if (sp.n <= 1) return bytes;
+    return bytes + 3 * (size_t)sp.n * B * H * S * D * sizeof(float);
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
@@ -79,9 +88,12 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const 
     const void *ptrs[] = {q, k, v, dout, lse, delta, dq, dk, dv, workspace};
     for (const void *p : ptrs)
         if (!aligned16(p)) return FA_EALIGN;
-    if (workspace_bytes < fa_bwd_workspace_size(B, H, S, D, dtype)) return FA_EWORKSPACE;
+    if (workspace_bytes < bwd_base_workspace(B, H, S)) return FA_EWORKSPACE;
+    // the split backward runs only when the workspace holds its partials
+    const bool split = workspace_bytes >= fa_bwd_workspace_size(B, H, S, D, dtype);
     return map_launch(fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv,
-                                     static_cast<float *>(workspace), B * H, S, D, scale, causal, stream));
+                                     static_cast<float *>(workspace), B * H, S, D, scale, causal, split,
+                                     stream));
 }
 
 int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, float *lse_parts,

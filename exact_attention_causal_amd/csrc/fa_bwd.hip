@@ -23,6 +23,8 @@
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
+#include <algorithm>
+
 namespace fa {
 
 // ---------------------------------------------------------------- delta ---
@@ -103,6 +105,11 @@ __global__ __launch_bounds__(256) void lse2_kernel(const float *__restrict__ lse
 struct BwdShape {
     int BH, Sq, Sk, off, causal, nqt, accumulate;
     float c, scale;  // c = scale * log2(e)
+    // key-set calls (GEN) may cut the reduction of a pass into chunks, one per
+    // blockIdx.y, each writing its own partial result: dK/dV over chunks of
+    // `qchunk` queries (partials BH*Sk*D elements apart), dQ over chunks of
+    // `kchunk` keys (BH*Sq*D apart).  One chunk each is the plain call.
+    int qchunk, kchunk;
 };
 
 // 8 consecutive gradient values of one lane, times `mul`, stored or (GEN)
@@ -477,21 +484,26 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
-    const int BH = a.BH, S = a.Sq, causal = a.causal;
-    const int Sk = GEN ? a.Sk : S;
-    const int off = GEN ? a.off : 0;
+    const int BH = a.BH, Sh = a.Sq, causal = a.causal;
+    // this launch's queries: chunk blockIdx.y of the head's query rows
+    // (uniform values kept in scalar registers, see the forward kernel)
+    const int qbeg = GEN ? blockIdx.y * a.qchunk : 0;
+    const int S = GEN ? __builtin_amdgcn_readfirstlane(min(a.qchunk, Sh - qbeg)) : Sh;
+    const int Sk = GEN ? a.Sk : Sh;
+    const int off = GEN ? __builtin_amdgcn_readfirstlane(a.off + qbeg) : 0;
     const float c = a.c;
     const int bid = blockIdx.x;
     const int kt = bid / BH;  // ascending: the tiles with the most query tiles go first
     const int bh = bid % BH;
-    q += (size_t)bh * S * D;
-    dout += (size_t)bh * S * D;
+    q += ((size_t)bh * Sh + qbeg) * D;
+    dout += ((size_t)bh * Sh + qbeg) * D;
     k += (size_t)bh * Sk * D;
     v += (size_t)bh * Sk * D;
-    dk += (size_t)bh * Sk * D;
-    dv += (size_t)bh * Sk * D;
-    lse += (size_t)bh * S;
-    delta += (size_t)bh * S;
+    const size_t part = GEN ? (size_t)blockIdx.y * BH * Sk * D : 0;
+    dk += part + (size_t)bh * Sk * D;
+    dv += part + (size_t)bh * Sk * D;
+    lse += (size_t)bh * Sh + qbeg;
+    delta += (size_t)bh * Sh + qbeg;
     const int k0 = kt * C::BKV;
     const int kw0 = k0 + wave * 32;
     const int key = kw0 + l32;  // this lane's key column
@@ -758,17 +770,21 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int BH = a.BH, S = a.Sq, causal = a.causal;
-    const int Sk = GEN ? a.Sk : S;    // keys of the head (queries: S)
-    const int off = GEN ? a.off : 0;  // query i sits off positions after key 0
+    // this launch's keys: chunk blockIdx.y of the head's key rows
+    const int kbeg = GEN ? blockIdx.y * a.kchunk : 0;
+    const int Skh = GEN ? a.Sk : S;  // keys per head (queries: S)
+    const int Sk = GEN ? __builtin_amdgcn_readfirstlane(min(a.kchunk, Skh - kbeg)) : S;
+    // query i sits off positions after key 0 of this launch
+    const int off = GEN ? __builtin_amdgcn_readfirstlane(a.off - kbeg) : 0;
     const float c = a.c;
     const int bid = blockIdx.x;
     const int qt = causal ? (a.nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
     q += (size_t)bh * S * D;
     dout += (size_t)bh * S * D;
-    dq += (size_t)bh * S * D;
-    k += (size_t)bh * Sk * D;
-    v += (size_t)bh * Sk * D;
+    dq += (GEN ? (size_t)blockIdx.y * BH * S * D : 0) + (size_t)bh * S * D;
+    k += ((size_t)bh * Skh + kbeg) * D;
+    v += ((size_t)bh * Skh + kbeg) * D;
     lse += (size_t)bh * S;
     delta += (size_t)bh * S;
     const int q0 = qt * C::BQ;
@@ -930,6 +946,22 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     }
 }
 
+// ---------------------------------------------- sum of partial results ---
+
+// out = sum of n fp32 partial results `stride` elements apart, in a fixed
+// order (so the split backward stays bit-reproducible), rounded to T; four
+// elements per thread (count4 = elements / 4).
+template <typename T>
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float *__restrict__ parts, int n,
+                                                        long long stride, T *__restrict__ out,
+                                                        long long count4) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count4) return;
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(parts + 4 * i);
+    for (int p = 1; p < n; ++p) acc += *reinterpret_cast<const f32x4 *>(parts + p * stride + 4 * i);
+    store4<T>(out + 4 * i, acc, 1.f);
+}
+
 // ------------------------------------------------------------- launches ---
 
 template <typename T, int D>
@@ -963,9 +995,12 @@ using KvTile1For = KvTile1<T, D, 8, sizeof(T) == 2 && D == 128, sizeof(T) == 2 ?
 template <typename T, int D>
 constexpr bool kv_single() { return sizeof(T) == 2; }
 
+// ny > 1 (key-set calls only): dK/dV over ny query chunks and dQ over ny key
+// chunks of a.qchunk / a.kchunk rows, side by side (blockIdx.y).
 template <typename T, int D, typename OutT, bool GEN>
 static int bwd_for(const void *q, const void *k, const void *v, const void *dout, const float *lse,
-                   const float *delta, OutT *dq, OutT *dk, OutT *dv, BwdShape a, hipStream_t stream) {
+                   const float *delta, OutT *dq, OutT *dk, OutT *dv, BwdShape a, hipStream_t stream,
+                   int ny = 1) {
     using KC = KvTileFor<T, D>;
     using K1 = KvTile1For<T, D>;
     using QC = QTileFor<T, D>;
@@ -973,15 +1008,16 @@ static int bwd_for(const void *q, const void *k, const void *v, const void *dout
     const long long g1 = (long long)((a.Sk + BKV - 1) / BKV) * a.BH;
     a.nqt = (a.Sq + QC::BQ - 1) / QC::BQ;
     const long long g2 = (long long)a.nqt * a.BH;
-    if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return -1;
+    if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL || ny < 1 || ny > 65535) return -1;
+    if (ny > 1 && !(GEN && kv_single<T, D>())) return -1;  // (the pair kernel takes no chunks)
     if constexpr (kv_single<T, D>())
-        hipLaunchKernelGGL((dkdv1_kernel<T, K1, OutT, GEN>), dim3((unsigned)g1), dim3(K1::NT), 0, stream,
+        hipLaunchKernelGGL((dkdv1_kernel<T, K1, OutT, GEN>), dim3((unsigned)g1, ny), dim3(K1::NT), 0, stream,
                            (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dk, dv, a);
     else
         hipLaunchKernelGGL((dkdv_kernel<T, KC, OutT, GEN>), dim3((unsigned)g1), dim3(KC::NT), 0, stream,
                            (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dk, dv, a);
     if (hipGetLastError() != hipSuccess) return -5;
-    hipLaunchKernelGGL((dq_kernel<T, QC, OutT, GEN>), dim3((unsigned)g2), dim3(QC::NT), 0, stream,
+    hipLaunchKernelGGL((dq_kernel<T, QC, OutT, GEN>), dim3((unsigned)g2, ny), dim3(QC::NT), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dq, a);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
@@ -995,6 +1031,22 @@ static int bwd_for(const void *q, const void *k, const void *v, const void *dout
     case 96: { constexpr int DD = 96; return CALL; }   \
     case 128: { constexpr int DD = 128; return CALL; } \
     default: return -2;                   \
+    }
+
+// (as FA_D_SWITCH, but falls through on success)
+#define FA_D_SWITCH_INT(D, CALL)                                          \
+    {                                                                      \
+        int rc_ = -2;                                                      \
+        switch (D) {                                                       \
+        case 16: { constexpr int DD = 16; rc_ = CALL; break; }             \
+        case 32: { constexpr int DD = 32; rc_ = CALL; break; }             \
+        case 64: { constexpr int DD = 64; rc_ = CALL; break; }             \
+        case 80: { constexpr int DD = 80; rc_ = CALL; break; }             \
+        case 96: { constexpr int DD = 96; rc_ = CALL; break; }             \
+        case 128: { constexpr int DD = 128; rc_ = CALL; break; }           \
+        default: break;                                                    \
+        }                                                                  \
+        if (rc_ != 0) return rc_;                                          \
     }
 
 template <typename T>
@@ -1017,17 +1069,58 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
     return -2;
 }
 
+BwdSplit bwd_split(int dtype, int BH, int S, int D) {
+    BwdSplit r{1, S};
+    if (dtype != 1 || !head_dim_supported(D) || S <= 256) return r;
+    // one wave of dK/dV workgroups (256 keys each) per CU or less: the
+    // longest causal tile walks the whole sequence alone
+    const long long tiles = (long long)BH * ((S + 255) / 256);
+    if (tiles >= 2 * kNumCU) return r;
+    long long n = (2 * kNumCU + tiles - 1) / tiles;
+    // at most 16 chunks, at most 256 MiB of partial results
+    const long long per = 3LL * BH * S * D * 4;
+    n = std::min<long long>(n, std::min<long long>(16, (256LL << 20) / per));
+    if (n < 2) return r;
+    const int chunk = (int)(((S + n - 1) / n + 63) / 64 * 64);  // whole 64-row tiles
+    r.n = (S + chunk - 1) / chunk;
+    r.chunk = chunk;
+    if (r.n < 2) r = BwdSplit{1, S};
+    return r;
+}
+
 int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
                const float *lse, const float *delta, void *dq, void *dk, void *dv, float *lse2, int BH,
-               int S, int D, float scale, int causal, hipStream_t stream) {
+               int S, int D, float scale, int causal, bool allow_split, hipStream_t stream) {
     if (dtype != 0 && dtype != 1) return -2;
     if (!head_dim_supported(D)) return -2;
+    const BwdSplit sp = allow_split ? bwd_split(dtype, BH, S, D) : BwdSplit{1, S};
+    if (sp.n > 1) {
+        // Few key tiles for the CUs: dK/dV over sp.n query chunks and dQ over
+        // sp.n key chunks run side by side as key-set products (natural-log L,
+        // fp32 partials in the workspace after the lse2 region), then summed.
+        const size_t n_el = (size_t)BH * S * D;
+        float *parts = lse2 + ((size_t)BH * S + 63) / 64 * 64;
+        float *pq = parts, *pk = parts + (size_t)sp.n * n_el, *pv = parts + 2 * (size_t)sp.n * n_el;
+        const BwdShape a{BH, S, S, 0, causal, 0, 0, scale * kLog2e, scale, sp.chunk, sp.chunk};
+        FA_D_SWITCH_INT(D, (bwd_for<bf16, DD, float, true>(q, k, v, dout, lse, delta, pq, pk, pv, a, stream, sp.n)))
+        const long long count4 = (long long)(n_el / 4);
+        const long long grid = (count4 + 255) / 256;
+        if (grid > 0x7fffffffLL) return -1;
+        float *const src[3] = {pq, pk, pv};
+        void *const dst[3] = {dq, dk, dv};
+        for (int t = 0; t < 3; ++t) {
+            hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3((unsigned)grid), dim3(256), 0, stream, src[t], sp.n,
+                               (long long)n_el, (bf16 *)dst[t], count4);
+            if (hipGetLastError() != hipSuccess) return -5;
+        }
+        return 0;
+    }
     const long long rows = (long long)BH * S;
     const long long grid = (rows + 255) / 256;
     if (grid > 0x7fffffffLL) return -1;
     hipLaunchKernelGGL(lse2_kernel, dim3((unsigned)grid), dim3(256), 0, stream, lse, lse2, rows);
     if (hipGetLastError() != hipSuccess) return -5;
-    const BwdShape a{BH, S, S, 0, causal, 0, 0, scale * kLog2e, scale};
+    const BwdShape a{BH, S, S, 0, causal, 0, 0, scale * kLog2e, scale, S, S};
     if (dtype == 1)
         return bwd_dispatch<bf16, bf16, false>(D, q, k, v, dout, lse2, delta, (bf16 *)dq, (bf16 *)dk,
                                                (bf16 *)dv, a, stream);
@@ -1039,7 +1132,7 @@ int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, c
                        const float *lse, const float *delta, float *dq, float *dk, float *dv,
                        int accumulate, int BH, int Sq, int Sk, int D, float scale, int causal,
                        int q_offset, hipStream_t stream) {
-    const BwdShape a{BH, Sq, Sk, q_offset, causal, 0, accumulate, scale * kLog2e, scale};
+    const BwdShape a{BH, Sq, Sk, q_offset, causal, 0, accumulate, scale * kLog2e, scale, Sq, Sk};
     if (dtype == 1)
         return bwd_dispatch<bf16, float, true>(D, q, k, v, dout, lse, delta, dq, dk, dv, a, stream);
     if (dtype == 0)

@@ -32,10 +32,19 @@ int launch_merge(int dtype, const float *o_parts, const float *lse_parts, int n,
 int launch_delta(int dtype, const void *o, const void *dout, float *delta, int BH, int S, int D,
                  hipStream_t stream);
 
-// lse2: BH*S floats of workspace for the base-2 copy of lse.
+// How the bf16 backward of a problem with few key tiles per CU is split: n
+// chunks of `chunk` rows per pass (n = 1: not split).
+struct BwdSplit {
+    int n, chunk;
+};
+BwdSplit bwd_split(int dtype, int BH, int S, int D);
+
+// lse2: workspace of at least BH*S floats (the base-2 copy of lse), rounded
+// up to 64 floats, followed -- when bwd_split gives n > 1 -- by 3*n*BH*S*D
+// floats of partial results (used only with allow_split).
 int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
                const float *lse, const float *delta, void *dq, void *dk, void *dv, float *lse2,
-               int BH, int S, int D, float scale, int causal, hipStream_t stream);
+               int BH, int S, int D, float scale, int causal, bool allow_split, hipStream_t stream);
 
 // Gradient contributions of one key set (fp32, stored or added).
 int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, const void *dout,

@@ -189,9 +189,12 @@ def backward(q, k, v, o, lse, dout, causal=True, scale=None, delta=None, grads=N
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
     _check(fa_bwd_preprocess(o, dout, delta, B, H, S, D, code, stream), "fa_bwd_preprocess")
-    ws_bytes = fa_bwd_workspace_size(B, H, S, D, code)
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    if workspace is None:
+        ws_bytes = fa_bwd_workspace_size(B, H, S, D, code)
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    else:  # a caller's workspace (a smaller one disables the split backward)
+        ws_bytes = workspace.numel() * workspace.element_size()
     _check(fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, ws_bytes, B, H, S, D, scale,
                   causal, code, stream), "fa_bwd")
     return dq, dk, dv, delta

@@ -85,9 +85,12 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
  * Bytes of device workspace fa_bwd needs for these sizes: B*H*S fp32 values
  * (rounded up to 256 bytes), where fa_bwd keeps lse in base 2 (L * log2 e)
  * so that recomputing P = 2^(S * scale * log2 e - L * log2 e) costs no
- * multiply per probability.  No partial sums are kept there: dK/dV and dQ
- * are each owned by one workgroup.  Returns 0 for invalid sizes; fa_bwd
- * reports those.
+ * multiply per probability.  For bf16 problems with too few key tiles to
+ * fill the GPU (B*H*ceil(S/256) below 512 and S > 256), fa_bwd can instead
+ * cut each pass into n chunks (n <= 16, 64-row multiples) that run side by
+ * side and sum their fp32 partial dQ, dK, dV in a fixed order (still
+ * bit-reproducible): the size returned then adds 3*n*B*H*S*D fp32 values (at
+ * most 256 MiB).  Returns 0 for invalid sizes; fa_bwd reports those.
  */
 size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
 
@@ -96,11 +99,14 @@ size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
  * probabilities recomputed from lse:
  *   q, k, v, dout : [B][H][S][D] inputs    lse, delta : [B][H][S] fp32 inputs
  *   dq, dk, dv    : [B][H][S][D] outputs
- *   workspace     : device scratch of at least fa_bwd_workspace_size() bytes,
- *                   16-byte aligned (FA_EWORKSPACE if smaller, FA_EINVAL if
- *                   NULL); its contents on entry do not matter and are
- *                   overwritten.  Calls that share one workspace must be
- *                   ordered on one stream.
+ *   workspace     : device scratch of fa_bwd_workspace_size() bytes,
+ *                   16-byte aligned (FA_EINVAL if NULL).  Its contents on
+ *                   entry do not matter and are overwritten.  Calls that
+ *                   share one workspace must be ordered on one stream.  A
+ *                   smaller workspace of at least B*H*S fp32 (rounded up to
+ *                   256 bytes) is accepted too: the backward is then not
+ *                   split (equal results up to the order of fp32 sums,
+ *                   slower on few-head problems); below that, FA_EWORKSPACE.
  * `scale` and `causal` must be the values the forward pass used.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *dout,

@@ -625,6 +625,32 @@ def test_rising_scores_wide_tile():
         assert absdiff(lse[:, hh:hh + 1].double().cpu().numpy(), r_l) <= TOL["bf16"]["lse"], hh
 
 
+@pytest.mark.parametrize("B,H,S,D,causal", [(1, 1, 300, 64, True), (1, 1, 1000, 80, True),
+                                             (1, 2, 4097, 128, True), (1, 1, 777, 16, False),
+                                             (2, 1, 2000, 96, True)])
+def test_split_backward(B, H, S, D, causal):
+    """bf16 problems with few key tiles per CU: the backward runs each pass in
+    chunks side by side and sums the fp32 partials (a fixed order, so still
+    bit-reproducible)."""
+    assert fa.fa_bwd_workspace_size(B, H, S, D, fa.FA_BF16) > ((B * H * S * 4 + 255) // 256) * 256
+    q, k, v, do = make_inputs(B, H, S, D, "bf16", seed=2100 + S)
+    check_full(q, k, v, do, "bf16", causal=causal, label=f"split backward B={B} H={H} S={S} D={D}")
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=causal)
+    first = fa.backward(qd, kd, vd, o, lse, dod, causal=causal)
+    again = fa.backward(qd, kd, vd, o, lse, dod, causal=causal)
+    for a_, b_ in zip(first, again):
+        assert torch.equal(a_, b_)
+    # a workspace holding only the base-2 L runs the unsplit backward: the same gradients
+    # up to the order of fp32 sums
+    small = torch.empty(((B * H * S * 4 + 255) // 256) * 256, device=dev, dtype=torch.uint8)
+    plain = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, workspace=small)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(first[:3], plain[:3]):
+        assert rel(a_.double().cpu().numpy(), b_.double().cpu().numpy()) <= 1e-2
+
+
 def test_first_query_and_identical_keys():
     """Closed forms on the GPU: O_0 = V_0; identical keys give the causal prefix mean."""
     S, D = 300, 64
