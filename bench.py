@@ -249,7 +249,8 @@ def sweep(dev):
                     n = 10 if S >= 16384 else 30
                     t_f, t_s, t_sp = timed(fwd, n), timed(step, n), timed(fwd_split, n)
                     # memory of one fwd+bwd step over the inputs already held: the
-                    # outputs, L and D (no S x S matrix exists at any point)
+                    # outputs, L, D and the backward's workspace (no S x S matrix
+                    # exists at any point)
                     del op, lp
                     torch.cuda.synchronize()
                     base = torch.cuda.memory_allocated()
@@ -259,7 +260,7 @@ def sweep(dev):
                     peak = (torch.cuda.max_memory_allocated() - base) / 2**20
                     # (this step's buffers were allocated before `base`; report all of them)
                     peak += sum(t.numel() * t.element_size()
-                                for t in (o, lse, delta, dq, dk, dv)) / 2**20
+                                for t in (o, lse, delta, dq, dk, dv, ws)) / 2**20
                     sxs = S * S * 4 / 2**20
                     pairs = S * (S + 1) // 2 if causal else S * S
                     tf_f = 4 * D * pairs / (t_f * 1e-3) / 1e12
