@@ -1077,9 +1077,10 @@ BwdSplit bwd_split(int dtype, int BH, int S, int D) {
     const long long tiles = (long long)BH * ((S + 255) / 256);
     if (tiles >= 2 * kNumCU) return r;
     long long n = (2 * kNumCU + tiles - 1) / tiles;
-    // at most 16 chunks, at most 256 MiB of partial results
+    // at most 8 chunks (16 were no faster overall and hold twice the
+    // partials), at most 256 MiB of partial results
     const long long per = 3LL * BH * S * D * 4;
-    n = std::min<long long>(n, std::min<long long>(16, (256LL << 20) / per));
+    n = std::min<long long>(n, std::min<long long>(8, (256LL << 20) / per));
     if (n < 2) return r;
     const int chunk = (int)(((S + n - 1) / n + 63) / 64 * 64);  // whole 64-row tiles
     r.n = (S + chunk - 1) / chunk;

@@ -87,7 +87,7 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
  * so that recomputing P = 2^(S * scale * log2 e - L * log2 e) costs no
  * multiply per probability.  For bf16 problems with too few key tiles to
  * fill the GPU (B*H*ceil(S/256) below 512 and S > 256), fa_bwd can instead
- * cut each pass into n chunks (n <= 16, 64-row multiples) that run side by
+ * cut each pass into n chunks (n <= 8, 64-row multiples) that run side by
  * side and sum their fp32 partial dQ, dK, dV in a fixed order (still
  * bit-reproducible): the size returned then adds 3*n*B*H*S*D fp32 values (at
  * most 256 MiB).  Returns 0 for invalid sizes; fa_bwd reports those.

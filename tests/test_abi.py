@@ -59,10 +59,10 @@ def test_workspace_size(lib):
     assert fa.fa_bwd_workspace_size(1, 1, 0, 64, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 128, 72, fa.FA_BF16) == 0
     # bf16 with fewer than 512 key tiles of 256 (S > 256): + 3*n*B*H*S*D fp32 partials of the
-    # split backward, n <= 16 chunks of whole 64-row tiles, at most 256 MiB of partials
-    assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_BF16) == 8192 * 4 + 3 * 16 * 8192 * 128 * 4
+    # split backward, n <= 8 chunks of whole 64-row tiles, at most 256 MiB of partials
+    assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_BF16) == 8192 * 4 + 3 * 8 * 8192 * 128 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 65536, 128, fa.FA_BF16) == 65536 * 4 + 3 * 2 * 65536 * 128 * 4
-    assert fa.fa_bwd_workspace_size(1, 1, 1000, 80, fa.FA_BF16) == 4096 + 3 * 16 * 1000 * 80 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 1000, 80, fa.FA_BF16) == 4096 + 3 * 8 * 1000 * 80 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_F32) == 8192 * 4          # fp32: never split
     assert fa.fa_bwd_workspace_size(2, 16, 8192, 128, fa.FA_BF16) == 32 * 8192 * 4   # enough tiles
 
