@@ -36,11 +36,16 @@
 
 namespace fa {
 
-template <typename T, int D_, int NQB_, int BK_, int NW_>
+// NG = 2 (problems with few query tiles): the waves form two groups that
+// share their queries and split the key tiles (group g takes tiles g, g+2,
+// ...), each with its own LDS ring; group 1 hands its (m, l, O) to group 0,
+// which merges and stores.  Halves the longest tile's key walk.
+template <typename T, int D_, int NQB_, int BK_, int NW_, int NG_ = 1>
 struct FwdTile {
     static constexpr int D = D_, NQB = NQB_, BK = BK_;
     static constexpr int NW = NW_, NT = NW * kWave;
-    static constexpr int BQ = NW * NQB * 32;          // queries per workgroup
+    static constexpr int NG = NG_, NWG = NW / NG;    // key groups, waves per group
+    static constexpr int BQ = NWG * NQB * 32;         // queries per workgroup
     static constexpr int KPL = Mma<T>::KPL;
     static constexpr int NSD = D / 2 / KPL;           // MFMAs over d per 32x32 block
     static constexpr int NKB = BK / 32;               // 32-key blocks per tile
@@ -48,9 +53,12 @@ struct FwdTile {
     static constexpr bool TAIL = KPL == 8 && D % 32 == 16;
     static constexpr int ND = TAIL ? D / 32 : (D + 31) / 32;  // 32-row output blocks over d
     static constexpr int NI = 16 / KPL;               // MFMAs per 32-key reduction block
-    using DMA = TileDma<T, D, BK, NW / 2>;           // half the waves load K, half V
+    using DMA = TileDma<T, D, BK, NWG / 2>;          // half a group's waves load K, half V
     static constexpr int TILE = DMA::ELEMS;           // elements per K or V tile
     static_assert(D % 16 == 0 && BK % 32 == 0 && NW % 2 == 0, "tile shape");
+    static_assert(NG == 1 || (NG == 2 && NQB == 1 && NWG % 2 == 0), "key groups");
+    // the merge hands 8 floats per lane at a time through the first K stage
+    static_assert(NG == 1 || TILE * (int)sizeof(T) >= NWG * kWave * 8 * 4, "merge buffer");
 };
 
 // The running maximum m may lag the scores: a tile whose probabilities
@@ -89,11 +97,14 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
     // Each stage is its own array and the loop is unrolled by three, so the
     // compiler can see that reads of one stage never alias the DMA into the
     // others and does not wait for the tiles in flight.
-    __shared__ __attribute__((aligned(1024))) T sK0[C::TILE], sK1[C::TILE], sK2[C::TILE];
-    __shared__ __attribute__((aligned(1024))) T sV0[C::TILE], sV1[C::TILE], sV2[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sK0[C::NG * C::TILE], sK1[C::NG * C::TILE], sK2[C::NG * C::TILE];
+    __shared__ __attribute__((aligned(1024))) T sV0[C::NG * C::TILE], sV1[C::NG * C::TILE], sV2[C::NG * C::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = C::NG == 1 ? 0 : wave_all / C::NWG;          // key group
+    const int wave = C::NG == 1 ? wave_all : wave_all % C::NWG;  // wave within its group
+    const int gofs = grp * C::TILE;                              // the group's LDS ring
     const int h = lane >> 5, l32 = lane & 31;
     const int BH = a.BH, S = a.Sq, causal = a.causal;
     const float c = a.c;
@@ -151,12 +162,13 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
     }
 
     typename C::DMA dma;
-    const int half = wave / (C::NW / 2), hw = wave % (C::NW / 2);
+    const int half = wave / (C::NWG / 2), hw = wave % (C::NWG / 2);
     dma.init(lane, hw);
     // this wave's share of key/value tile j: K (first half of the waves) or V
     auto issue = [&](T *nK, T *nV, int j) { dma.issue(half ? nV : nK, half ? v : k, j * BK, Sk, hw); };
-    issue(sK0, sV0, 0);
-    issue(sK1, sV1, 1);
+    // the group's tiles: grp, grp + NG, grp + 2 NG, ...
+    issue(sK0 + gofs, sV0 + gofs, grp);
+    issue(sK1 + gofs, sV1 + gofs, C::NG + grp);
 
     // The prefetch of a tile goes out one instruction at a time, spread over a
     // step's work (parts: one before each S^T block and each O^T block).  It
@@ -165,7 +177,7 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
     // wait for every DMA before the next LDS read.
     constexpr int NP = 2 * C::NKB;
     auto rs = C::DMA::range(k, 0, 0);  // range of the tile being prefetched
-    T *nT = sK2;                       // and the stage it lands in
+    T *nT = sK2 + gofs;                // and the stage it lands in
     auto part = [&](int p) {
         if (p >= 0) dma.issue_part(p, NP, nT, rs, hw);
     };
@@ -326,11 +338,12 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
             }
         }
     };
-    // start of step j: tile j has landed everywhere, then tile j+2 is aimed at (nK, nV)
+    // start of step j: tile j has landed everywhere, then the group's tile
+    // two steps on (j + 2 NG) is aimed at (nK, nV)
     auto begin_step = [&](T *nK, T *nV, int j) {
-        wait_vmcnt<C::DMA::IPW>();  // this wave's part of tile j has landed (j+1 may be in flight)
-        lds_barrier();              // every part of it; the stage tile j+2 goes to is released
-        rs = C::DMA::range(half ? v : k, (j + 2) * BK, Sk);
+        wait_vmcnt<C::DMA::IPW>();  // this wave's part of tile j has landed (the next may be in flight)
+        lds_barrier();              // every part of it; the stage the next-but-one tile goes to is released
+        rs = C::DMA::range(half ? v : k, (j + 2 * C::NG) * BK, Sk);
         nT = half ? nV : nK;
     };
 
@@ -347,12 +360,74 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
         }
         wait_lgkm0();  // this wave's reads of the stage are complete before the next barrier
     };
-    for (int j = 0; j < nkt; j += 3) {
-        step(sK0, sV0, sK2, sV2, j);
-        if (j + 1 < nkt) step(sK1, sV1, sK0, sV0, j + 1);
-        if (j + 2 < nkt) step(sK2, sV2, sK1, sV1, j + 2);
+    // (every wave runs the same number of steps; a group's tile past nkt is inactive)
+    const int nst = (nkt + C::NG - 1) / C::NG;
+    for (int t = 0; t < nst; t += 3) {
+        step(sK0 + gofs, sV0 + gofs, sK2 + gofs, sV2 + gofs, C::NG * t + grp);
+        if (t + 1 < nst) step(sK1 + gofs, sV1 + gofs, sK0 + gofs, sV0 + gofs, C::NG * (t + 1) + grp);
+        if (t + 2 < nst) step(sK2 + gofs, sV2 + gofs, sK1 + gofs, sV1 + gofs, C::NG * (t + 2) + grp);
     }
     wait_vmcnt<0>();  // no DMA may still be writing this workgroup's LDS when it exits
+
+    if constexpr (C::NG == 2) {
+        // Group 1 hands its (m, l, O^T) to group 0 through the first K stage,
+        // 8 floats per lane at a time; group 0 rescales both to the larger m
+        // and adds (O and l of either half share that half's m).
+        float *xb = reinterpret_cast<float *>(sK0) + wave * kWave + lane;
+        constexpr int XS = C::NWG * kWave;  // floats per handed register
+        auto hand = [&](auto put, auto take) {
+            lds_barrier();  // the stage is free (all reads done)
+            if (grp == 1) put();
+            lds_barrier();
+            if (grp == 0) take();
+        };
+        float a0 = 1.f, a1 = 0.f;
+        hand([&] { xb[0] = mrow[0]; xb[XS] = lrow[0]; },
+             [&] {
+                 const float m1 = xb[0], l1 = xb[XS];
+                 const float m0 = mrow[0];
+                 const float mn = fmaxf(m0, m1);
+                 // (a half that saw no key has m = -inf and l = 0: weight 0)
+                 a0 = (m0 == -INFINITY) ? 0.f : fast_exp2(m0 - mn);
+                 a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mn);
+                 lrow[0] = a0 * lrow[0] + a1 * l1;
+                 mrow[0] = mn;
+             });
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr)
+                hand([&] {
+#pragma unroll
+                         for (int t = 0; t < 8; ++t) xb[t * XS] = acc[0][db][8 * hr + t];
+                     },
+                     [&] {
+#pragma unroll
+                         for (int t = 0; t < 8; ++t)
+                             acc[0][db][8 * hr + t] = a0 * acc[0][db][8 * hr + t] + a1 * xb[t * XS];
+                     });
+        if constexpr (C::TAIL) {
+            // tail lanes hold queries of other lanes: their factors come by the same swap
+            float b0, b1, c0, c1;
+            tail_cols(a0, b0, b1);
+            tail_cols(a1, c0, c1);
+            hand([&] {
+#pragma unroll
+                     for (int t = 0; t < 4; ++t) {
+                         xb[t * XS] = tacc[0][0][t];
+                         xb[(4 + t) * XS] = tacc[0][1][t];
+                     }
+                 },
+                 [&] {
+#pragma unroll
+                     for (int t = 0; t < 4; ++t) {
+                         tacc[0][0][t] = b0 * tacc[0][0][t] + c0 * xb[t * XS];
+                         tacc[0][1][t] = b1 * tacc[0][1][t] + c1 * xb[(4 + t) * XS];
+                     }
+                 });
+        }
+        if (grp == 1) return;
+    }
 
     // Epilogue: O = acc / l, L = (m + log2 l) * ln 2 (natural log of the scaled scores).
 #pragma unroll
@@ -403,10 +478,23 @@ static int run_fwd(const void *q, const void *k, const void *v, OutT *o, float *
 template <typename T, int D>
 constexpr int fwd_bk() { return (sizeof(T) == 4 && D > 80) ? 32 : 64; }
 
+// Key tiles of the two-group tile (bf16, D >= 64): its LDS holds two rings.
+template <int D>
+constexpr int fwd_bk2() { return D > 80 ? 32 : 64; }
+
 template <typename T, int D, typename OutT, bool GEN>
 static int fwd_for(const void *q, const void *k, const void *v, OutT *o, float *lse, const FwdShape &a,
                    int n_split, hipStream_t stream) {
     constexpr int BK = fwd_bk<T, D>();
+    // At most one 256-query tile per CU: two key groups per workgroup on
+    // 128-query tiles (the longest tile walks half the keys per group).
+    // Measured 1.4-1.9x faster there (one head, S = 1024 to 65536; four heads
+    // at S = 16384), 10 % slower at two tiles per CU.
+    if constexpr (sizeof(T) == 2 && D >= 64 && !GEN) {
+        const long long tiles1 = (long long)((a.Sq + 255) / 256) * a.BH;
+        if (tiles1 <= kNumCU)
+            return run_fwd<T, FwdTile<T, D, 1, fwd_bk2<D>(), 8, 2>, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    }
     // bf16 D=128: 64 queries per wave over 32-key tiles halves the K/V reads
     // per FLOP, but makes the query tiles twice as long; keep it for problems
     // with at least four such tiles per CU (short causal problems lose more
@@ -475,6 +563,10 @@ FA_FWD_HEAD(float, 80)
 FA_FWD_HEAD(float, 96)
 FA_FWD_HEAD(float, 128)
 FA_FWD_KERNEL(bf16, FwdTile<bf16 COMMA 128 COMMA 2 COMMA 32 COMMA 8>, bf16, false)
+FA_FWD_KERNEL(bf16, FwdTile<bf16 COMMA 64 COMMA 1 COMMA fwd_bk2<64>() COMMA 8 COMMA 2>, bf16, false)
+FA_FWD_KERNEL(bf16, FwdTile<bf16 COMMA 80 COMMA 1 COMMA fwd_bk2<80>() COMMA 8 COMMA 2>, bf16, false)
+FA_FWD_KERNEL(bf16, FwdTile<bf16 COMMA 96 COMMA 1 COMMA fwd_bk2<96>() COMMA 8 COMMA 2>, bf16, false)
+FA_FWD_KERNEL(bf16, FwdTile<bf16 COMMA 128 COMMA 1 COMMA fwd_bk2<128>() COMMA 8 COMMA 2>, bf16, false)
 #undef FA_FWD_HEAD
 #undef FA_FWD_KERNEL
 #undef COMMA

@@ -628,11 +628,12 @@ def test_rising_scores_wide_tile():
 @pytest.mark.parametrize("B,H,S,D,causal", [(1, 1, 300, 64, True), (1, 1, 1000, 80, True),
                                              (1, 2, 4097, 128, True), (1, 1, 777, 16, False),
                                              (2, 1, 2000, 96, True), (1, 1, 257, 128, True),
-                                             (3, 1, 520, 64, True)])
+                                             (3, 1, 520, 64, True), (1, 1, 8192, 64, True)])
 def test_split_backward(B, H, S, D, causal):
     """bf16 problems with few key tiles per CU: the backward runs each pass in
     chunks side by side and sums the fp32 partials (a fixed order, so still
-    bit-reproducible)."""
+    bit-reproducible); the forward of these shapes (D >= 64) runs two key
+    groups per workgroup and merges them."""
     assert fa.fa_bwd_workspace_size(B, H, S, D, fa.FA_BF16) > ((B * H * S * 4 + 255) // 256) * 256
     q, k, v, do = make_inputs(B, H, S, D, "bf16", seed=2100 + S)
     check_full(q, k, v, do, "bf16", causal=causal, label=f"split backward B={B} H={H} S={S} D={D}")
