@@ -38,7 +38,7 @@ DEFAULT_WORKLOAD = "bf16_b1h16_s65536_d128"
 # rocprofv3 --pmc passes (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a
 # plain 1 GiB copy calibrates; see profiles/), keyed by a hash of the forward
 # kernel's sources: once those change, the figure is stale and reported as null.
-FWD_TRAFFIC = {"sources_sha1": "96e7fdc4c3e3ffb957170c3af781c56255164d54", "bytes": 9507919552}
+FWD_TRAFFIC = {"sources_sha1": "70b9e8d3cfc902e2d062537e758cff9f7cbf548d", "bytes": 9507919552}
 FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp")
 
 

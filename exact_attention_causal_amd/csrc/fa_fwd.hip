@@ -486,15 +486,15 @@ template <typename T, int D, typename OutT, bool GEN>
 static int fwd_for(const void *q, const void *k, const void *v, OutT *o, float *lse, const FwdShape &a,
                    int n_split, hipStream_t stream) {
     constexpr int BK = fwd_bk<T, D>();
-    // At most 1.5 256-query tiles per CU: two key groups per workgroup on
-    // 128-query tiles (the longest tile walks half the keys per group).
-    // Measured 1.4-1.9x faster at one tile per CU or fewer (one head,
-    // S = 1024 to 65536; four heads at S = 16384), 1-13 % faster at 1.25 to
-    // 1.5 (most at D = 64 and 80; level at D = 96 and 128), 10 % slower at
-    // 1.75 and 2.
+    // Few 256-query tiles per CU: two key groups per workgroup on 128-query
+    // tiles (the longest tile walks half the keys per group). Measured
+    // 1.4-1.9x faster at one tile per CU or fewer (one head, S = 1024 to
+    // 65536; four heads at S = 16384). Past that, D = 64 and 80 gain 9-14 %
+    // up to two tiles per CU and are level at 2.5; D = 96 and 128 are level
+    // at 1.5 and 10 % slower at 1.75 and 2.
     if constexpr (sizeof(T) == 2 && D >= 64 && !GEN) {
         const long long tiles1 = (long long)((a.Sq + 255) / 256) * a.BH;
-        if (2 * tiles1 <= 3 * kNumCU)
+        if (D <= 80 ? tiles1 <= 2 * kNumCU : 2 * tiles1 <= 3 * kNumCU)
             return run_fwd<T, FwdTile<T, D, 1, fwd_bk2<D>(), 8, 2>, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
     }
     // bf16 D=128: 64 queries per wave over 32-key tiles halves the K/V reads

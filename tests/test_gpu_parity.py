@@ -212,12 +212,14 @@ def test_sequence_tails_wide_heads(S, D):
 
 @pytest.mark.parametrize("H,S,D,causal", [(1, 700, 64, False), (2, 333, 96, False), (1, 1, 128, False),
                                           (3, 100, 80, False), (1, 40, 128, True),
-                                          (128, 512, 128, True), (192, 512, 128, True), (193, 512, 128, True)])
+                                          (128, 512, 128, True), (192, 512, 128, True), (193, 512, 128, True),
+                                          (256, 512, 64, True), (257, 512, 64, True)])
 def test_two_key_groups(H, S, D, causal):
-    # a bf16 forward with at most 1.5 256-query tiles per CU (D >= 64) splits each 128-query tile's
-    # keys over two wave groups and merges their m, l and O at the end: one key tile (the second
-    # group has none), non-causal rows, ragged tails; 192 heads x 512 rows is the largest such
-    # launch (384 tiles), 193 x 512 the smallest past it (one group)
+    # a bf16 forward with few 256-query tiles per CU (D >= 64) splits each 128-query tile's keys
+    # over two wave groups and merges their m, l and O at the end: one key tile (the second group
+    # has none), non-causal rows, ragged tails; at D = 128, 192 heads x 512 rows is the largest
+    # such launch (384 tiles, 1.5 per CU), 193 x 512 the smallest past it (one group); at D = 64
+    # the limit is 512 tiles (256 heads)
     q, k, v, do = make_inputs(1, H, S, D, "bf16", seed=2100 + H + S + D)
     check_full(q, k, v, do, "bf16", causal=causal, label=f"two key groups H={H} S={S} D={D} causal={causal}")
 
