@@ -53,7 +53,7 @@ WORKLOADS = {
     ]
 }
 
-#: seed for the sampled row set of the long-context workload
+#: seed for the sampled heads and rows of the long workloads
 ROW_SAMPLE_SEED = 1005
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -80,12 +80,20 @@ def workload_inputs(w: Workload):
     return make_inputs(w.B, w.H, w.S, w.D, w.dtype, w.seed, w.qk_mult)
 
 
-def sample_rows(n_heads, S, n, seed=ROW_SAMPLE_SEED, tile=128):
-    """Seeded (head, row) sample: always holds row 0, row S-1 and a tile edge."""
+def sample_head_rows(n_heads, S, heads=4, per_head=64, seed=ROW_SAMPLE_SEED):
+    """Seeded rows of a few heads: [(head, sorted rows)], `heads` distinct heads with
+    `per_head` distinct rows each.  Every head's rows hold the ends of the sequence
+    (0, 1, S-2, S-1), the edges of 32-, 256- and 512-row tiles at the start, the
+    last 256-row tile edge, and random rows for the rest."""
     g = torch.Generator("cpu").manual_seed(int(seed))
-    heads = torch.randint(0, n_heads, (n,), generator=g)
-    rows = torch.randint(0, S, (n,), generator=g)
-    fixed = [0, S - 1, min(tile, S - 1), min(tile - 1, S - 1)]
-    for t, r in enumerate(fixed[:n]):
-        rows[t] = r
-    return [(int(h), int(r)) for h, r in zip(heads.tolist(), rows.tolist())]
+    hs = torch.randperm(n_heads, generator=g)[:min(heads, n_heads)].tolist()
+    last = (S - 1) // 256 * 256
+    fixed = [0, 1, 31, 32, 255, 256, 511, 512, last - 1, last, S - 2, S - 1]
+    out = []
+    for h in sorted(hs):
+        rows = {r for r in fixed if 0 <= r < S}
+        want = min(per_head, S)
+        while len(rows) < want:
+            rows.update(torch.randint(0, S, (want - len(rows),), generator=g).tolist())
+        out.append((int(h), sorted(rows)))
+    return out
