@@ -5,10 +5,42 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa.h"
 #include "fa_launch.hpp"
 
+namespace fa {
+
 namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu[kMaxDevices];  // 0: not read yet
+}  // namespace
+
+int stream_cu_count(hipStream_t stream) {
+    int dev = -1;
+    if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return 0;
+    int n = g_cu[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    g_cu[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace fa
+
+namespace {
+
+// Compute units a size query assumes when no device is visible: those of one
+// MI355X.  (Launches always read the count of the device they run on.)
+constexpr int kAssumedCU = 256;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -50,7 +82,12 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     if (int rc = check_shape(B, H, S, D, dtype)) return rc;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return FA_EALIGN;
-    return map_launch(fa::launch_fwd(dtype, q, k, v, o, lse, B * H, S, D, scale, causal, stream));
+    // one workgroup per 256 queries of every head must fit a launch grid (the
+    // 512-query tile needs fewer; the 128-query one is chosen only for small grids)
+    if ((long long)((S + 255) / 256) * B * H > 0x7fffffffLL) return FA_EINVAL;
+    const int ncu = fa::stream_cu_count(stream);
+    if (ncu <= 0) return FA_EHIP;
+    return map_launch(fa::launch_fwd(dtype, q, k, v, o, lse, B * H, S, D, scale, causal, ncu, stream));
 }
 
 int fa_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int S, int D,
@@ -61,39 +98,68 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int 
     return map_launch(fa::launch_delta(dtype, o, dout, delta, B * H, S, D, stream));
 }
 
-// The part of the backward workspace every call needs: the base-2 copy of
-// lse, one fp32 per row, rounded up to 256 bytes.
-static size_t bwd_base_workspace(int B, int H, int S) {
-    return ((size_t)B * H * S * sizeof(float) + 255) & ~(size_t)255;
-}
-
 size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype) {
     if (check_shape(B, H, S, D, dtype) != FA_OK) return 0;
-    const size_t bytes = bwd_base_workspace(B, H, S);
+    const long long BH = (long long)B * H;
     // bf16 problems with few key tiles per CU: fp32 partial dQ, dK, dV of
-    // each chunk of the split backward
-    const fa::BwdSplit sp = fa::bwd_split(dtype, B * H, S, D);
-    if (sp.n <= 1) return bytes;
-    return bytes + 3 * (size_t)sp.n * B * H * S * D * sizeof(float);
+    // each chunk of the split backward, for the current device's CU count
+    int ncu = fa::stream_cu_count(nullptr);
+    if (ncu <= 0) ncu = kAssumedCU;
+    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, ncu, fa::kMaxSplitBytes);
+    return fa::bwd_lse2_bytes(BH * S) + fa::bwd_part_bytes(sp, BH, S, D);
+}
+
+// Argument checks of fa_bwd.
+static int check_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+                     const float *delta, void *dq, void *dk, void *dv, int B, int H, int S, int D, float scale,
+                     int causal, fa_dtype dtype) {
+    if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv) return FA_EINVAL;
+    if (causal != 0 && causal != 1) return FA_EINVAL;
+    if (int rc = check_scale(scale)) return rc;
+    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
+    const void *ptrs[] = {q, k, v, dout, lse, delta, dq, dk, dv};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return FA_EALIGN;
+    // one workgroup per 128 keys of every head (the smallest key tile) must fit a launch grid
+    if ((long long)((S + 127) / 128) * B * H > 0x7fffffffLL) return FA_EINVAL;
+    return FA_OK;
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
            const float *delta, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
            int B, int H, int S, int D, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
-    if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv) return FA_EINVAL;
-    if (causal != 0 && causal != 1) return FA_EINVAL;
-    if (int rc = check_scale(scale)) return rc;
-    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
+    if (int rc = check_bwd(q, k, v, dout, lse, delta, dq, dk, dv, B, H, S, D, scale, causal, dtype)) return rc;
     if (!workspace) return FA_EINVAL;
-    const void *ptrs[] = {q, k, v, dout, lse, delta, dq, dk, dv, workspace};
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return FA_EALIGN;
-    if (workspace_bytes < bwd_base_workspace(B, H, S)) return FA_EWORKSPACE;
-    // the split backward runs only when the workspace holds its partials
-    const bool split = workspace_bytes >= fa_bwd_workspace_size(B, H, S, D, dtype);
+    if (!aligned16(workspace)) return FA_EALIGN;
+    const long long BH = (long long)B * H;
+    const size_t base = fa::bwd_lse2_bytes(BH * S);
+    if (workspace_bytes < base) return FA_EWORKSPACE;
+    const int ncu = fa::stream_cu_count(stream);
+    if (ncu <= 0) return FA_EHIP;
+    // the split backward takes as many chunks as the workspace holds partials for
+    const size_t budget = workspace_bytes - base < fa::kMaxSplitBytes ? workspace_bytes - base : fa::kMaxSplitBytes;
+    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, ncu, budget);
     return map_launch(fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv,
-                                     static_cast<float *>(workspace), B * H, S, D, scale, causal, split,
-                                     stream));
+                                     static_cast<float *>(workspace), (int)BH, S, D, scale, causal, sp, stream));
+}
+
+int fa_get_plan(int B, int H, int S, int D, fa_dtype dtype, int num_cu, fa_plan *plan) {
+    if (!plan) return FA_EINVAL;
+    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
+    if (num_cu <= 0) {
+        num_cu = fa::stream_cu_count(nullptr);
+        if (num_cu <= 0) return FA_EHIP;
+    }
+    const int BH = B * H;
+    const fa::FwdPlan f = fa::fwd_plan(dtype, BH, S, D, num_cu);
+    const fa::BwdSplit sp = fa::bwd_split(dtype, BH, S, D, num_cu, fa::kMaxSplitBytes);
+    plan->num_cu = num_cu;
+    plan->fwd_block_queries = f.bq;
+    plan->fwd_key_groups = f.groups;
+    plan->fwd_key_tile = f.bk;
+    plan->bwd_chunks = sp.n;
+    plan->bwd_chunk_rows = sp.chunk;
+    return FA_OK;
 }
 
 int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, float *lse_parts,
@@ -161,7 +227,7 @@ const char *fa_strerror(int status) {
     case FA_EUNSUPPORTED: return "unsupported head dimension or dtype";
     case FA_EALIGN: return "pointer not 16-byte aligned";
     case FA_EWORKSPACE: return "workspace too small";
-    case FA_EHIP: return "HIP kernel launch failed";
+    case FA_EHIP: return "HIP runtime error (no device visible, device query or kernel launch failed)";
     default: return "unknown status";
     }
 }

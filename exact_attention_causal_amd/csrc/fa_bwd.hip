@@ -1069,18 +1069,19 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
     return -2;
 }
 
-BwdSplit bwd_split(int dtype, int BH, int S, int D) {
+BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_bytes) {
     BwdSplit r{1, S};
     if (dtype != 1 || !head_dim_supported(D) || S <= 256) return r;
+    const long long cu = ncu > 0 ? ncu : 1;
     // one wave of dK/dV workgroups (256 keys each) per CU or less: the
     // longest causal tile walks the whole sequence alone
     const long long tiles = (long long)BH * ((S + 255) / 256);
-    if (tiles >= 2 * kNumCU) return r;
-    long long n = (2 * kNumCU + tiles - 1) / tiles;
+    if (tiles >= 2 * cu) return r;
+    long long n = (2 * cu + tiles - 1) / tiles;
     // at most 8 chunks (16 were no faster overall and hold twice the
-    // partials), at most 256 MiB of partial results
+    // partials), and no more partial results than the budget
     const long long per = 3LL * BH * S * D * 4;
-    n = std::min<long long>(n, std::min<long long>(8, (256LL << 20) / per));
+    n = std::min<long long>(n, std::min<long long>(8, (long long)(max_part_bytes / (size_t)per)));
     if (n < 2) return r;
     const int chunk = (int)(((S + n - 1) / n + 63) / 64 * 64);  // whole 64-row tiles
     r.n = (S + chunk - 1) / chunk;
@@ -1091,16 +1092,16 @@ BwdSplit bwd_split(int dtype, int BH, int S, int D) {
 
 int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
                const float *lse, const float *delta, void *dq, void *dk, void *dv, float *lse2, int BH,
-               int S, int D, float scale, int causal, bool allow_split, hipStream_t stream) {
+               int S, int D, float scale, int causal, BwdSplit sp, hipStream_t stream) {
     if (dtype != 0 && dtype != 1) return -2;
     if (!head_dim_supported(D)) return -2;
-    const BwdSplit sp = allow_split ? bwd_split(dtype, BH, S, D) : BwdSplit{1, S};
     if (sp.n > 1) {
+        if (dtype != 1) return -1;  // (bwd_split splits bf16 problems only)
         // Few key tiles for the CUs: dK/dV over sp.n query chunks and dQ over
         // sp.n key chunks run side by side as key-set products (natural-log L,
         // fp32 partials in the workspace after the lse2 region), then summed.
         const size_t n_el = (size_t)BH * S * D;
-        float *parts = lse2 + ((size_t)BH * S + 63) / 64 * 64;
+        float *parts = lse2 + bwd_lse2_bytes((long long)BH * S) / sizeof(float);
         float *pq = parts, *pk = parts + (size_t)sp.n * n_el, *pv = parts + 2 * (size_t)sp.n * n_el;
         const BwdShape a{BH, S, S, 0, causal, 0, 0, scale * kLog2e, scale, sp.chunk, sp.chunk};
         FA_D_SWITCH_INT(D, (bwd_for<bf16, DD, float, true>(q, k, v, dout, lse, delta, pq, pk, pv, a, stream, sp.n)))

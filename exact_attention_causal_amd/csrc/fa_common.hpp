@@ -41,7 +41,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWave = 64;
-constexpr int kNumCU = 256;  // compute units of one MI355X (launch-shape heuristics only)
 
 template <typename T> struct Mma;
 

@@ -375,11 +375,18 @@ __global__ __launch_bounds__(C::NT, (!GEN && C::D == 80 && C::KPL == 8 && C::NQB
         // and adds (O and l of either half share that half's m).
         float *xb = reinterpret_cast<float *>(sK0) + wave * kWave + lane;
         constexpr int XS = C::NWG * kWave;  // floats per handed register
+        // lds_barrier() does not wait for this wave's LDS accesses (the
+        // hardware does not either), so each side waits for its own before
+        // the barrier that publishes them: group 1's writes must have landed
+        // before group 0 reads, and group 0's reads must be done before the
+        // next round's writes reuse the buffer.
         auto hand = [&](auto put, auto take) {
-            lds_barrier();  // the stage is free (all reads done)
+            lds_barrier();  // the buffer is free (every earlier read done)
             if (grp == 1) put();
-            lds_barrier();
+            wait_lgkm0();
+            lds_barrier();  // the writes are visible
             if (grp == 0) take();
+            wait_lgkm0();
         };
         float a0 = 1.f, a1 = 0.f;
         hand([&] { xb[0] = mrow[0]; xb[XS] = lrow[0]; },
@@ -482,52 +489,75 @@ constexpr int fwd_bk() { return (sizeof(T) == 4 && D > 80) ? 32 : 64; }
 template <int D>
 constexpr int fwd_bk2() { return D > 80 ? 32 : 64; }
 
-template <typename T, int D, typename OutT, bool GEN>
-static int fwd_for(const void *q, const void *k, const void *v, OutT *o, float *lse, const FwdShape &a,
-                   int n_split, hipStream_t stream) {
-    constexpr int BK = fwd_bk<T, D>();
+FwdPlan fwd_plan(int dtype, int BH, int S, int D, int ncu) {
+    const bool bf = dtype == 1;
+    const long long cu = ncu > 0 ? ncu : 1;
     // Few 256-query tiles per CU: two key groups per workgroup on 128-query
     // tiles (the longest tile walks half the keys per group). Measured
     // 1.4-1.9x faster at one tile per CU or fewer (one head, S = 1024 to
     // 65536; four heads at S = 16384). Past that, D = 64 and 80 gain 9-14 %
     // up to two tiles per CU and are level at 2.5; D = 96 and 128 are level
     // at 1.5 and 10 % slower at 1.75 and 2.
-    if constexpr (sizeof(T) == 2 && D >= 64 && !GEN) {
-        const long long tiles1 = (long long)((a.Sq + 255) / 256) * a.BH;
-        if (D <= 80 ? tiles1 <= 2 * kNumCU : 2 * tiles1 <= 3 * kNumCU)
-            return run_fwd<T, FwdTile<T, D, 1, fwd_bk2<D>(), 8, 2>, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    if (bf && D >= 64) {
+        const long long tiles1 = (long long)((S + 255) / 256) * BH;
+        if (D <= 80 ? tiles1 <= 2 * cu : 2 * tiles1 <= 3 * cu) return FwdPlan{128, 2, D > 80 ? 32 : 64};
     }
     // bf16 D=128: 64 queries per wave over 32-key tiles halves the K/V reads
     // per FLOP, but makes the query tiles twice as long; keep it for problems
     // with at least four such tiles per CU (short causal problems lose more
     // to the uneven tile lengths than they gain).  Measured slower at D=80.
-    using C2 = FwdTile<T, D, 2, 32, 8>;
-    if constexpr (sizeof(T) == 2 && D == 128 && !GEN) {
-        const long long tiles2 = (long long)((a.Sq + C2::BQ - 1) / C2::BQ) * a.BH;
-        if (tiles2 >= 4 * kNumCU) return run_fwd<T, C2, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    if (bf && D == 128) {
+        const long long tiles2 = (long long)((S + 511) / 512) * BH;
+        if (tiles2 >= 4 * cu) return FwdPlan{512, 1, 32};
     }
-    return run_fwd<T, FwdTile<T, D, 1, BK, 8>, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    return FwdPlan{256, 1, (!bf && D > 80) ? 32 : 64};
+}
+
+// Launch tile C if it is the one the plan names.
+template <typename T, typename C, typename OutT, bool GEN>
+static bool pick(const FwdPlan &p, int &rc, const void *q, const void *k, const void *v, OutT *o, float *lse,
+                 const FwdShape &a, int n_split, hipStream_t stream) {
+    if (p.bq != C::BQ || p.groups != C::NG || p.bk != C::BK) return false;
+    rc = run_fwd<T, C, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    return true;
+}
+
+template <typename T, int D, typename OutT, bool GEN>
+static int fwd_for(const void *q, const void *k, const void *v, OutT *o, float *lse, const FwdShape &a,
+                   int n_split, int ncu, hipStream_t stream) {
+    using C1 = FwdTile<T, D, 1, fwd_bk<T, D>(), 8>;
+    // shifted / split keys: always the 256-query tile
+    if constexpr (GEN) return run_fwd<T, C1, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    const FwdPlan p = fwd_plan(sizeof(T) == 2 ? 1 : 0, a.BH, a.Sq, D, ncu);
+    int rc = -5;
+    if constexpr (!GEN && sizeof(T) == 2 && D >= 64)
+        if (pick<T, FwdTile<T, D, 1, fwd_bk2<D>(), 8, 2>, OutT, GEN>(p, rc, q, k, v, o, lse, a, n_split, stream))
+            return rc;
+    if constexpr (!GEN && sizeof(T) == 2 && D == 128)
+        if (pick<T, FwdTile<T, D, 2, 32, 8>, OutT, GEN>(p, rc, q, k, v, o, lse, a, n_split, stream)) return rc;
+    if (pick<T, C1, OutT, GEN>(p, rc, q, k, v, o, lse, a, n_split, stream)) return rc;
+    return -5;  // (a plan with no matching tile: fwd_plan and the tiles disagree)
 }
 
 template <typename T, bool GEN, typename OutT>
 static int fwd_dispatch(int D, const void *q, const void *k, const void *v, OutT *o, float *lse,
-                        const FwdShape &a, int n_split, hipStream_t stream) {
+                        const FwdShape &a, int n_split, int ncu, hipStream_t stream) {
     switch (D) {
-    case 16: return fwd_for<T, 16, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
-    case 32: return fwd_for<T, 32, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
-    case 64: return fwd_for<T, 64, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
-    case 80: return fwd_for<T, 80, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
-    case 96: return fwd_for<T, 96, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
-    case 128: return fwd_for<T, 128, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
+    case 16: return fwd_for<T, 16, OutT, GEN>(q, k, v, o, lse, a, n_split, ncu, stream);
+    case 32: return fwd_for<T, 32, OutT, GEN>(q, k, v, o, lse, a, n_split, ncu, stream);
+    case 64: return fwd_for<T, 64, OutT, GEN>(q, k, v, o, lse, a, n_split, ncu, stream);
+    case 80: return fwd_for<T, 80, OutT, GEN>(q, k, v, o, lse, a, n_split, ncu, stream);
+    case 96: return fwd_for<T, 96, OutT, GEN>(q, k, v, o, lse, a, n_split, ncu, stream);
+    case 128: return fwd_for<T, 128, OutT, GEN>(q, k, v, o, lse, a, n_split, ncu, stream);
     default: return -2;
     }
 }
 
 int launch_fwd(int dtype, const void *q, const void *k, const void *v, void *o, float *lse, int BH,
-               int S, int D, float scale, int causal, hipStream_t stream) {
+               int S, int D, float scale, int causal, int ncu, hipStream_t stream) {
     FwdShape a{BH, S, S, 0, S, causal, 0, scale * kLog2e, 0, 0};
-    if (dtype == 1) return fwd_dispatch<bf16, false>(D, q, k, v, (bf16 *)o, lse, a, 1, stream);
-    if (dtype == 0) return fwd_dispatch<float, false>(D, q, k, v, (float *)o, lse, a, 1, stream);
+    if (dtype == 1) return fwd_dispatch<bf16, false>(D, q, k, v, (bf16 *)o, lse, a, 1, ncu, stream);
+    if (dtype == 0) return fwd_dispatch<float, false>(D, q, k, v, (float *)o, lse, a, 1, ncu, stream);
     return -2;
 }
 
@@ -536,8 +566,8 @@ int launch_fwd_partial(int dtype, const void *q, const void *k, const void *v, f
                        int q_offset, int n_split, int chunk, hipStream_t stream) {
     FwdShape a{BH, Sq, Sk, q_offset, chunk, causal, 0, scale * kLog2e, (long long)BH * Sq * D,
                (long long)BH * Sq};
-    if (dtype == 1) return fwd_dispatch<bf16, true>(D, q, k, v, o_parts, lse_parts, a, n_split, stream);
-    if (dtype == 0) return fwd_dispatch<float, true>(D, q, k, v, o_parts, lse_parts, a, n_split, stream);
+    if (dtype == 1) return fwd_dispatch<bf16, true>(D, q, k, v, o_parts, lse_parts, a, n_split, 0, stream);
+    if (dtype == 0) return fwd_dispatch<float, true>(D, q, k, v, o_parts, lse_parts, a, n_split, 0, stream);
     return -2;
 }
 

@@ -15,10 +15,24 @@ inline bool head_dim_supported(int D) {
     return false;
 }
 
+// Compute units of the device a launch on `stream` runs on (the null stream:
+// the current device), read from the runtime once per device and cached; 0
+// if no device is visible.  Every launch-shape threshold below takes it as an
+// argument.
+int stream_cu_count(hipStream_t stream);
+
+// Forward tile configuration of a self-attention problem: queries per
+// workgroup, key groups per workgroup (2: two wave groups split the key tiles
+// and merge) and keys per LDS tile.
+struct FwdPlan {
+    int bq, groups, bk;
+};
+FwdPlan fwd_plan(int dtype, int BH, int S, int D, int ncu);
+
 // Each returns 0 on success, -2 (unsupported D/dtype) or -5 (launch refused).
-// Sizes are already validated; BH = B*H.
+// Sizes are already validated; BH = B*H; ncu as stream_cu_count.
 int launch_fwd(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
-               int BH, int S, int D, float scale, int causal, hipStream_t stream);
+               int BH, int S, int D, float scale, int causal, int ncu, hipStream_t stream);
 
 // Shifted / split-key forward with fp32 partial outputs; `chunk` keys per split.
 int launch_fwd_partial(int dtype, const void *q, const void *k, const void *v, float *o_parts,
@@ -33,18 +47,27 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
                  hipStream_t stream);
 
 // How the bf16 backward of a problem with few key tiles per CU is split: n
-// chunks of `chunk` rows per pass (n = 1: not split).
+// chunks of `chunk` rows per pass (n = 1: not split), with at most
+// `max_part_bytes` of fp32 partial results.
 struct BwdSplit {
     int n, chunk;
 };
-BwdSplit bwd_split(int dtype, int BH, int S, int D);
+constexpr size_t kMaxSplitBytes = (size_t)256 << 20;  // partials of the caller-workspace backward
+BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_bytes);
 
-// lse2: workspace of at least BH*S floats (the base-2 copy of lse), rounded
-// up to 64 floats, followed -- when bwd_split gives n > 1 -- by 3*n*BH*S*D
-// floats of partial results (used only with allow_split).
+// Bytes of the base-2 copy of lse at the start of the backward workspace (one
+// fp32 per row, rounded up to 256 bytes); the split's partials follow it.
+inline size_t bwd_lse2_bytes(long long rows) { return ((size_t)rows * sizeof(float) + 255) & ~(size_t)255; }
+// Bytes of the partials of a split into sp.n chunks.
+inline size_t bwd_part_bytes(const BwdSplit &sp, long long BH, int S, int D) {
+    return sp.n <= 1 ? 0 : 3 * (size_t)sp.n * BH * S * D * sizeof(float);
+}
+
+// lse2: workspace of bwd_lse2_bytes(BH*S), followed -- when sp.n > 1 -- by
+// bwd_part_bytes(sp, ...) of partial results.  sp comes from bwd_split.
 int launch_bwd(int dtype, const void *q, const void *k, const void *v, const void *dout,
                const float *lse, const float *delta, void *dq, void *dk, void *dv, float *lse2,
-               int BH, int S, int D, float scale, int causal, bool allow_split, hipStream_t stream);
+               int BH, int S, int D, float scale, int causal, BwdSplit sp, hipStream_t stream);
 
 // Gradient contributions of one key set (fp32, stored or added).
 int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, const void *dout,

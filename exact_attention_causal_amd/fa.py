@@ -1,7 +1,8 @@
 """ctypes binding of the gfx950 attention library (include/fa.h).
 
 The functions named like the C entry points (fa_fwd, fa_bwd_preprocess,
-fa_bwd_workspace_size, fa_bwd, fa_fwd_partial, fa_merge, fa_bwd_partial, fa_strerror) only marshal arguments: tensors
+fa_bwd_workspace_size, fa_bwd, fa_fwd_partial, fa_merge, fa_bwd_partial,
+fa_get_plan, fa_strerror) only marshal arguments: tensors
 become device pointers, the stream becomes HIP's stream handle, and the status
 code comes back unchanged.  ``forward`` / ``backward`` / ``attention_fwd_bwd``
 are conveniences that allocate outputs with PyTorch (device memory is the
@@ -37,6 +38,16 @@ _i = ctypes.c_int
 _f = ctypes.c_float
 
 
+class Plan(ctypes.Structure):
+    """fa_plan: the tile configuration the library picks for a problem (include/fa.h)."""
+    _fields_ = [("num_cu", ctypes.c_int), ("fwd_block_queries", ctypes.c_int),
+                ("fwd_key_groups", ctypes.c_int), ("fwd_key_tile", ctypes.c_int),
+                ("bwd_chunks", ctypes.c_int), ("bwd_chunk_rows", ctypes.c_int)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
 class FaError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
@@ -67,6 +78,8 @@ def load_library():
     lib.fa_merge.restype = _i
     lib.fa_bwd_partial.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _i, _i, _i, _vp]
     lib.fa_bwd_partial.restype = _i
+    lib.fa_get_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(Plan)]
+    lib.fa_get_plan.restype = _i
     lib.fa_strerror.argtypes = [_i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -113,6 +126,13 @@ def fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes, B,
                                  int(dtype), _stream(stream))
 
 
+def fa_get_plan(B, H, S, D, dtype, num_cu=0):
+    """(status, Plan) for a problem on a device with num_cu compute units (0: the current one)."""
+    plan = Plan()
+    rc = load_library().fa_get_plan(B, H, S, D, int(dtype), int(num_cu), ctypes.byref(plan))
+    return rc, plan
+
+
 def fa_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Sq, Sk, D, scale, causal, q_offset, n_split,
                    dtype, stream=None):
     return load_library().fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o_parts), _ptr(lse_parts),
@@ -153,16 +173,54 @@ def _check(status, where):
 
 
 def _shape(q):
-    if q.dim() != 4:
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("expected [B, H, S, D] tensors")
-    if not q.is_cuda:
-        raise ValueError("tensors must be on a GPU (there is no CPU path)")
     return tuple(q.shape)
 
 
+def _like(name, x, shape, dtype, device, contiguous=False):
+    """Raise ValueError unless x has this shape, dtype and device (and, for a buffer the
+    library writes into, is contiguous): the kernels take every size from q, so a
+    mismatched tensor would be read or written out of its bounds."""
+    if not isinstance(x, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+    if x.dtype != dtype:
+        raise ValueError(f"{name} has dtype {x.dtype}, expected {dtype}")
+    if x.device != device:
+        raise ValueError(f"{name} is on {x.device}, expected {device}")
+    if contiguous and not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (the library writes it in place)")
+
+
+def _on_gpu(x):
+    if not x.is_cuda:
+        raise ValueError("tensors must be on a GPU (there is no CPU path)")
+
+
+def _workspace(workspace, device):
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace.numel() * workspace.element_size()
+
+
 def forward(q, k, v, causal=True, scale=None, out=None, lse=None, stream=None):
-    """O, L for contiguous [B, H, S, D] q, k, v (bf16 or fp32) on the GPU."""
+    """O, L for [B, H, S, D] q, k, v (bf16 or fp32, same shape) on the GPU.
+
+    A caller's ``out`` ([B, H, S, D], q's dtype) and ``lse`` ([B, H, S] fp32) must be
+    contiguous tensors on q's device; they are overwritten.
+    """
     B, H, S, D = _shape(q)
+    code = dtype_code(q.dtype)
+    for n, x in (("k", k), ("v", v)):
+        _like(n, x, q.shape, q.dtype, q.device)
+    if out is not None:
+        _like("out", out, q.shape, q.dtype, q.device, contiguous=True)
+    if lse is not None:
+        _like("lse", lse, (B, H, S), torch.float32, q.device, contiguous=True)
+    _on_gpu(q)
     q, k, v = (x.contiguous() for x in (q, k, v))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -170,17 +228,34 @@ def forward(q, k, v, causal=True, scale=None, out=None, lse=None, stream=None):
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, S), device=q.device, dtype=torch.float32)
-    _check(fa_fwd(q, k, v, out, lse, B, H, S, D, scale, causal, dtype_code(q.dtype), stream),
-           "fa_fwd")
+    _check(fa_fwd(q, k, v, out, lse, B, H, S, D, scale, causal, code, stream), "fa_fwd")
     return out, lse
 
 
 def backward(q, k, v, o, lse, dout, causal=True, scale=None, delta=None, grads=None,
              workspace=None, stream=None):
-    """dQ, dK, dV (and delta) for the forward pass that produced o, lse."""
+    """dQ, dK, dV (and delta) for the forward pass that produced o, lse.
+
+    q, k, v, o, dout share one shape and dtype; lse is [B, H, S] fp32.  A caller's
+    ``delta`` ([B, H, S] fp32), ``grads`` (three tensors shaped and typed like q) and
+    ``workspace`` must be contiguous tensors on q's device.
+    """
     B, H, S, D = _shape(q)
-    q, k, v, o, dout = (x.contiguous() for x in (q, k, v, o, dout))
     code = dtype_code(q.dtype)
+    for n, x in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _like(n, x, q.shape, q.dtype, q.device)
+    _like("lse", lse, (B, H, S), torch.float32, q.device)
+    if delta is not None:
+        _like("delta", delta, (B, H, S), torch.float32, q.device, contiguous=True)
+    if grads is not None:
+        if len(grads) != 3:
+            raise ValueError("grads must be (dq, dk, dv)")
+        for n, x in zip(("dq", "dk", "dv"), grads):
+            _like(n, x, q.shape, q.dtype, q.device, contiguous=True)
+    if workspace is not None:
+        ws_bytes = _workspace(workspace, q.device)
+    _on_gpu(q)
+    q, k, v, o, dout, lse = (x.contiguous() for x in (q, k, v, o, dout, lse))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if delta is None:
@@ -193,8 +268,7 @@ def backward(q, k, v, o, lse, dout, causal=True, scale=None, delta=None, grads=N
         ws_bytes = fa_bwd_workspace_size(B, H, S, D, code)
         if ws_bytes:
             workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
-    else:  # a caller's workspace (a smaller one disables the split backward)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    # (a caller's smaller workspace disables the split backward)
     _check(fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, ws_bytes, B, H, S, D, scale,
                   causal, code, stream), "fa_bwd")
     return dq, dk, dv, delta
@@ -205,6 +279,17 @@ def split_chunk(Sk, n_split):
     return 64 * ((Sk + 64 * n_split - 1) // (64 * n_split))
 
 
+def _keys(q, k, v):
+    """Sk of key/value tensors that match q [B, H, Sq, D] in B, H, D, dtype and device."""
+    B, H, _, D = _shape(q)
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("expected [B, H, Sk, D] keys")
+    Sk = k.shape[2]
+    for n, x in (("k", k), ("v", v)):
+        _like(n, x, (B, H, Sk, D), q.dtype, q.device)
+    return Sk
+
+
 def forward_partial(q, k, v, causal=True, scale=None, q_offset=0, n_split=1, stream=None):
     """fp32 (O, L) of q [B,H,Sq,D] over each key chunk of k, v [B,H,Sk,D].
 
@@ -212,26 +297,32 @@ def forward_partial(q, k, v, causal=True, scale=None, q_offset=0, n_split=1, str
     sits q_offset positions after key 0 (see fa_fwd_partial in include/fa.h).
     """
     B, H, Sq, D = _shape(q)
-    Sk = k.shape[2]
+    code = dtype_code(q.dtype)
+    Sk = _keys(q, k, v)
+    _on_gpu(q)
     q, k, v = (x.contiguous() for x in (q, k, v))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o_parts = torch.empty((n_split, B, H, Sq, D), device=q.device, dtype=torch.float32)
     lse_parts = torch.empty((n_split, B, H, Sq), device=q.device, dtype=torch.float32)
     _check(fa_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Sq, Sk, D, scale, causal, q_offset,
-                          n_split, dtype_code(q.dtype), stream), "fa_fwd_partial")
+                          n_split, code, stream), "fa_fwd_partial")
     return o_parts, lse_parts
 
 
 def merge(o_parts, lse_parts, dtype=torch.bfloat16, stream=None):
     """Merge [n, B, H, S, D] fp32 partial outputs and [n, B, H, S] L into (O in dtype, L)."""
+    if not isinstance(o_parts, torch.Tensor) or o_parts.dim() != 5:
+        raise ValueError("expected [n, B, H, S, D] partial outputs")
     n, B, H, S, D = o_parts.shape
-    if not o_parts.is_cuda:
-        raise ValueError("tensors must be on a GPU (there is no CPU path)")
+    code = dtype_code(dtype)
+    _like("o_parts", o_parts, o_parts.shape, torch.float32, o_parts.device)
+    _like("lse_parts", lse_parts, (n, B, H, S), torch.float32, o_parts.device)
+    _on_gpu(o_parts)
     o_parts, lse_parts = o_parts.contiguous(), lse_parts.contiguous()
     o = torch.empty((B, H, S, D), device=o_parts.device, dtype=dtype)
     lse = torch.empty((B, H, S), device=o_parts.device, dtype=torch.float32)
-    _check(fa_merge(o_parts, lse_parts, n, o, lse, B, H, S, D, dtype_code(dtype), stream), "fa_merge")
+    _check(fa_merge(o_parts, lse_parts, n, o, lse, B, H, S, D, code, stream), "fa_merge")
     return o, lse
 
 
@@ -250,22 +341,29 @@ def backward_partial(q, k, v, dout, lse, delta, causal=True, scale=None, q_offse
     (fp32) the contributions are added to them; otherwise new tensors are returned.
     """
     B, H, Sq, D = _shape(q)
-    Sk = k.shape[2]
+    code = dtype_code(q.dtype)
+    Sk = _keys(q, k, v)
+    _like("dout", dout, q.shape, q.dtype, q.device)
+    _like("lse", lse, (B, H, Sq), torch.float32, q.device)
+    _like("delta", delta, (B, H, Sq), torch.float32, q.device)
+    accumulate = grads is not None
+    if grads is not None:
+        if len(grads) != 3:
+            raise ValueError("grads must be (dq, dk, dv)")
+        for n, x, shp in zip(("dq", "dk", "dv"), grads, ((B, H, Sq, D), (B, H, Sk, D), (B, H, Sk, D))):
+            _like(n, x, shp, torch.float32, q.device, contiguous=True)
+    _on_gpu(q)
     q, k, v, dout = (x.contiguous() for x in (q, k, v, dout))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    accumulate = grads is not None
     if grads is None:
         f32 = dict(device=q.device, dtype=torch.float32)
         grads = (torch.empty((B, H, Sq, D), **f32), torch.empty((B, H, Sk, D), **f32),
                  torch.empty((B, H, Sk, D), **f32))
     dq, dk, dv = grads
-    for g in grads:
-        if g.dtype != torch.float32 or not g.is_contiguous():
-            raise ValueError("gradient accumulators must be contiguous fp32 tensors")
     _check(fa_bwd_partial(q, k, v, dout, lse.contiguous(), delta.contiguous(), dq, dk, dv,
                           accumulate, B, H, Sq, Sk, D, scale, causal, q_offset,
-                          dtype_code(q.dtype), stream), "fa_bwd_partial")
+                          code, stream), "fa_bwd_partial")
     return dq, dk, dv
 
 

@@ -22,15 +22,16 @@
  * and the queries' offset from key 0 separately.
  *
  * Ownership.  The caller allocates every buffer (including the backward
- * workspace); the library never allocates, frees,
- * copies to or from the host, or synchronises.  Outputs are fully
- * overwritten; inputs must not alias outputs.  All pointers must be device
- * pointers aligned to 16 bytes.
+ * workspace); the library never allocates, frees, copies to or from the
+ * host, or synchronises.  Outputs are fully overwritten; inputs must not
+ * alias outputs.  All pointers must be device pointers aligned to 16 bytes.
  *
  * Streams and errors.  All work is enqueued on `stream` (0 = the null
  * stream).  Argument errors are returned synchronously, before anything is
  * enqueued.  Faults inside a kernel surface at the caller's next stream
- * synchronisation.  The library holds no mutable state and is thread-safe.
+ * synchronisation.  Launch shapes depend on the compute-unit count of the
+ * stream's device, read once per device and cached.  The library is
+ * thread-safe.
  *
  * Supported shapes.  D in {16, 32, 64, 80, 96, 128}; dtype FA_F32 or FA_BF16
  * (bf16 storage, bf16 matrix-core products with fp32 accumulation; the
@@ -57,8 +58,9 @@ enum {
     FA_EINVAL = -1,       /* null pointer, B/H/S <= 0, causal not 0/1, scale <= 0 or not finite, size overflow */
     FA_EUNSUPPORTED = -2, /* D or dtype not built */
     FA_EALIGN = -3,       /* a pointer is not 16-byte aligned */
-    FA_EWORKSPACE = -4,   /* workspace smaller than fa_bwd_workspace_size() */
-    FA_EHIP = -5          /* the HIP runtime refused a launch */
+    FA_EWORKSPACE = -4,   /* workspace below B*H*S fp32 values (see fa_bwd) */
+    FA_EHIP = -5          /* the HIP runtime failed: no device visible for the stream,
+                             a device query failed, or a launch was refused */
 };
 
 /*
@@ -86,11 +88,13 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
  * (rounded up to 256 bytes), where fa_bwd keeps lse in base 2 (L * log2 e)
  * so that recomputing P = 2^(S * scale * log2 e - L * log2 e) costs no
  * multiply per probability.  For bf16 problems with too few key tiles to
- * fill the GPU (B*H*ceil(S/256) below 512 and S > 256), fa_bwd can instead
- * cut each pass into n chunks (n <= 8, 64-row multiples) that run side by
- * side and sum their fp32 partial dQ, dK, dV in a fixed order (still
- * bit-reproducible): the size returned then adds 3*n*B*H*S*D fp32 values (at
- * most 256 MiB).  Returns 0 for invalid sizes; fa_bwd reports those.
+ * fill the GPU (B*H*ceil(S/256) below twice the device's compute units, and
+ * S > 256), fa_bwd can instead cut each pass into n chunks (n <= 8, 64-row
+ * multiples) that run side by side and sum their fp32 partial dQ, dK, dV in
+ * a fixed order (still bit-reproducible): the size returned then adds
+ * 3*n*B*H*S*D fp32 values (at most 256 MiB).  The compute-unit count is the
+ * current device's (that of one MI355X, 256, when no device is visible).
+ * Returns 0 for invalid sizes; fa_bwd reports those.
  */
 size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
 
@@ -104,9 +108,11 @@ size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
  *                   entry do not matter and are overwritten.  Calls that
  *                   share one workspace must be ordered on one stream.  A
  *                   smaller workspace of at least B*H*S fp32 (rounded up to
- *                   256 bytes) is accepted too: the backward is then not
- *                   split (equal results up to the order of fp32 sums,
- *                   slower on few-head problems); below that, FA_EWORKSPACE.
+ *                   256 bytes) is accepted too: the split backward then
+ *                   takes only as many chunks as it holds partials for, and
+ *                   none below two (equal results up to the order of fp32
+ *                   sums, slower on few-head problems); below that,
+ *                   FA_EWORKSPACE.
  * `scale` and `causal` must be the values the forward pass used.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *dout,
@@ -182,6 +188,24 @@ int fa_bwd_partial(const void *q, const void *k, const void *v, const void *dout
                    const float *lse, const float *delta, float *dq_acc, float *dk_acc,
                    float *dv_acc, int accumulate, int B, int H, int Sq, int Sk, int D,
                    float scale, int causal, int q_offset, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * The tile configuration fa_fwd and fa_bwd choose for a problem (handout,
+ * leaderboard problem: the tile sizes are tuned to the shape), for a device
+ * with num_cu compute units (num_cu <= 0: the current device's; FA_EHIP if
+ * none is visible).  Launches use the count of the device they run on.
+ */
+typedef struct {
+    int num_cu;             /* compute units the plan was made for */
+    int fwd_block_queries;  /* queries per forward workgroup: 128, 256 or 512 */
+    int fwd_key_groups;     /* 2: two wave groups split the key tiles and merge; else 1 */
+    int fwd_key_tile;       /* keys per LDS tile of the forward */
+    int bwd_chunks;         /* chunks of the split backward (1: not split), with a
+                               workspace of fa_bwd_workspace_size() bytes */
+    int bwd_chunk_rows;     /* rows per chunk (S when not split) */
+} fa_plan;
+
+int fa_get_plan(int B, int H, int S, int D, fa_dtype dtype, int num_cu, fa_plan *plan);
 
 /* Static, human-readable text for a status code. */
 const char *fa_strerror(int status);

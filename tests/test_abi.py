@@ -34,8 +34,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_partial", "fa_bwd_preprocess", "fa_bwd_workspace_size",
-                                     "fa_fwd", "fa_fwd_partial", "fa_merge", "fa_strerror"]
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_partial", "fa_bwd_preprocess",
+                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_partial", "fa_get_plan",
+                                     "fa_merge", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, -5):
-        assert fa.fa_strerror(code)
+        assert fa.fa_strerror(code) and "unknown" not in fa.fa_strerror(code)
     assert fa.fa_strerror(0) == "success"
     assert "unknown" in fa.fa_strerror(17)
 
@@ -193,3 +194,50 @@ def test_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+def _plan(B, H, S, D, dtype, ncu):
+    rc, p = fa.fa_get_plan(B, H, S, D, dtype, ncu)
+    assert rc == fa.FA_OK, fa.fa_strerror(rc)
+    assert p.num_cu == ncu
+    return p
+
+
+def test_plan_thresholds_follow_the_cu_count(lib):
+    """Tile selection is a function of the device's compute units: every threshold moves with them."""
+    bf, f32 = fa.FA_BF16, fa.FA_F32
+    # S=65536, D=128, 16 heads: 2048 tiles of 512 queries = 8 per CU on 256 CUs (64 queries per
+    # wave); below 4 per CU (1024 CUs) the 256-query tile; at 1.5 tiles of 256 per CU or fewer
+    # (3072 CUs and up) two key groups on 128-query tiles
+    assert (_plan(1, 16, 65536, 128, bf, 256).fwd_block_queries, _plan(1, 16, 65536, 128, bf, 256).fwd_key_tile) == (512, 32)
+    assert _plan(1, 16, 65536, 128, bf, 512).fwd_block_queries == 512    # exactly 4 per CU
+    assert _plan(1, 16, 65536, 128, bf, 513).fwd_block_queries == 256
+    assert _plan(1, 16, 65536, 128, bf, 2730).fwd_key_groups == 1        # 4096 > 1.5 * 2730
+    p = _plan(1, 16, 65536, 128, bf, 2731)
+    assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile) == (128, 2, 32)
+    # D <= 80: two key groups up to 2 tiles of 256 per CU (32 heads of 16000: 2016 tiles)
+    assert _plan(1, 32, 16000, 80, bf, 1007).fwd_key_groups == 1
+    p = _plan(1, 32, 16000, 80, bf, 1008)
+    assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile) == (128, 2, 64)
+    p = _plan(1, 32, 16000, 80, bf, 256)
+    assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile) == (256, 1, 64)
+    # fp32 never takes the bf16-only tiles; wide fp32 heads use 32-key tiles
+    p = _plan(1, 1, 4096, 128, f32, 256)
+    assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile, p.bwd_chunks) == (256, 1, 32, 1)
+    # split backward: below 2 dK/dV tiles of 256 keys per CU, n = ceil(2 CU / tiles) <= 8 chunks
+    p = _plan(1, 1, 8192, 128, bf, 256)          # 32 tiles: 16 wanted, 8 allowed
+    assert (p.bwd_chunks, p.bwd_chunk_rows) == (8, 1024)
+    p = _plan(1, 1, 8192, 128, bf, 32)           # 32 tiles: 2 wanted
+    assert (p.bwd_chunks, p.bwd_chunk_rows) == (2, 4096)
+    assert _plan(1, 1, 8192, 128, bf, 16).bwd_chunks == 1   # already 2 tiles per CU
+    p = _plan(1, 1, 65536, 128, bf, 256)         # 256 tiles: 2 wanted, 2 fit in 256 MiB
+    assert (p.bwd_chunks, p.bwd_chunk_rows) == (2, 32768)
+    assert _plan(1, 1, 65536, 128, bf, 128).bwd_chunks == 1
+    assert _plan(1, 1, 65536, 128, bf, 4096).bwd_chunks == 2     # 32 wanted; the partials cap at 2
+    assert _plan(1, 16, 65536, 128, bf, 4096).bwd_chunks == 1    # partials of 2 chunks: 1.5 GiB
+
+
+def test_plan_rejects(lib):
+    assert fa.fa_get_plan(1, 1, 0, 64, fa.FA_BF16, 256)[0] == fa.FA_EINVAL
+    assert fa.fa_get_plan(1, 1, 128, 72, fa.FA_BF16, 256)[0] == fa.FA_EUNSUPPORTED
+    assert fa.load_library().fa_get_plan(1, 1, 128, 64, 1, 256, None) == fa.FA_EINVAL
