@@ -33,6 +33,8 @@ METRIC = "causal attention fwd & fwd+bwd TFLOP/s (bf16) + % of MFMA peak, 1 GPU"
 PEAK_BF16 = 2516.6   # TFLOP/s, dense bf16 matrix cores (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_F32 = 157.3     # TFLOP/s, dense fp32 matrix cores
 DEFAULT_WORKLOAD = "bf16_b1h16_s65536_d128"
+# the other workload with a throughput target (S >= 16k), timed beside the headline one
+EXTRA_WORKLOADS = ("bf16_b1h32_s16000_d80",)
 
 # HBM traffic of one forward-kernel launch on the default workload, from two
 # rocprofv3 --pmc passes (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a
@@ -58,6 +60,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --workload (not also the other long workload)")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the sampled oracle check of the timed step's outputs")
     ap.add_argument("--cpu-tokens", type=int, default=12288,
                     help="sequence prefix the CPU oracle baseline runs on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -97,9 +103,60 @@ def cpu_baseline(w, q, k, v, do, tokens):
     dt = time.perf_counter() - t0
     pairs = w.B * w.H * S * (S + 1) // 2
     return {"value": 14 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": dt,
+            "kind": "oracle", "seconds": dt, "cpu_model": cpu_model(),
             "sample": f"fp64 oracle fwd+bwd on the first {S} tokens of all {w.B * w.H} heads "
                       f"(causal prefix of the same Q/K/V/dO), 14*D*pairs FLOPs / wall time"}
+
+
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it, read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def sampled_errors(w, cpu_in, outs, heads=1, per_head=64):
+    """Errors of one step's outputs against the fp64 oracle on seeded rows of a few heads.
+
+    O, L and dQ at the sampled query rows, dK and dV at the same key rows (with the
+    oracle's own L and D for every row of the sampled heads); max |gpu - oracle| /
+    max |oracle| per tensor, L in absolute terms.
+    """
+    import numpy as np
+    import oracle
+    from exact_attention_causal_amd.inputs import sample_head_rows
+    BH = w.B * w.H
+    qn, kn, vn, don = (x.reshape(BH, w.S, w.D) for x in cpu_in)
+    samples = sample_head_rows(BH, w.S, heads, per_head)
+    ref = {n: [] for n in ("o", "lse", "dq", "dk", "dv")}
+    got = {n: [] for n in ref}
+    for hh, rows in samples:
+        qh, kh, vh, dh = (x[hh].double().numpy() for x in (qn, kn, vn, don))
+        lse_full, del_full = oracle.head_stats(qh, kh, vh, dh, scale=w.scale)
+        o, lse, dq = oracle.rows(qh, kh, vh, dh, rows, scale=w.scale)
+        dk, dv = oracle.cols(qh, kh, vh, dh, lse_full, del_full, rows, scale=w.scale)
+        for n, r in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+            ref[n].append(r)
+            t = outs[n].reshape(BH, w.S, -1)[hh][rows] if n != "lse" else outs[n].reshape(BH, w.S)[hh][rows]
+            got[n].append(t.double().cpu().numpy())
+    err = {}
+    for n in ref:
+        a, b = np.concatenate(got[n]), np.concatenate(ref[n])
+        d = float(np.max(np.abs(a - b)))
+        err[n] = d if n == "lse" else d / float(np.max(np.abs(b)))
+    tol = {"o": 2e-2, "lse": 1e-3, "dq": 5e-2, "dk": 5e-2, "dv": 5e-2} if w.dtype == "bf16" else \
+        {"o": 1e-4, "lse": 1e-3, "dq": 1e-4, "dk": 1e-4, "dv": 1e-4}
+    return {"max_err": {n: float(f"{e:.3e}") for n, e in err.items()},
+            "tolerance": tol, "within_tolerance": all(err[n] <= tol[n] for n in err),
+            "sample": f"{len(samples)} seeded head(s) x {per_head} rows (sequence ends and tile edges "
+                      f"included) of the last timed step; O, L, dQ at those query rows, dK, dV at "
+                      f"the same key rows; errors relative to the oracle's max |x| (L absolute)",
+            "heads": [h for h, _ in samples]}
 
 
 def log(msg):
@@ -176,6 +233,41 @@ def split_kv(dev, w, n_split, steps, warmup, with_cpu):
                                "sample": f"fp64 oracle merge of the same {n_split} parts for {hs} of "
                                          f"{B * H} heads"}
     print(json.dumps(rec), flush=True)
+
+
+def hold(dev, w, seconds, entry):
+    """Run one entry point (fa_fwd, or fa_bwd_preprocess + fa_bwd) back to back for `seconds`
+    (to sample clocks and board power beside it) and print the mean time per call."""
+    fa.load_library()
+    code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+    B, H, S, D = w.shape
+    q, k, v, do = (x.to(dev) for x in workload_inputs(w))
+    o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_workspace_size(B, H, S, D, code)
+    ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+
+    def f():
+        if entry == "fwd":
+            rc = fa.fa_fwd(q, k, v, o, lse, B, H, S, D, w.scale, 1, code, sh)
+        else:
+            rc = fa.fa_bwd_preprocess(o, do, delta, B, H, S, D, code, sh) or \
+                fa.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, ws, ws_bytes, B, H, S, D, w.scale, 1, code, sh)
+        if rc != 0:
+            raise RuntimeError(fa.fa_strerror(rc))
+
+    f()
+    torch.cuda.synchronize()
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        n += 5
+    print(json.dumps({"hold_entry": entry, "calls": n,
+                      "ms_per_call": round((time.perf_counter() - t0) * 1e3 / n, 3)}), flush=True)
 
 
 def sweep(dev):
@@ -369,12 +461,40 @@ def main():
     if args.vs_materialised:
         vs_materialised(dev)
         return
+    if args.hold > 0:
+        hold(dev, WORKLOADS[args.workload], args.hold, args.hold_entry)
+        return
     if args.split_kv:
         split_kv(dev, WORKLOADS[args.workload], args.split_kv, args.steps, args.warmup,
                  not args.no_cpu_baseline)
         return
-    w = WORKLOADS[args.workload]
     fa.load_library()
+    w = WORKLOADS[args.workload]
+    rec, cpu_in, outs = time_workload(dev, w, args.steps, args.warmup, headline=True)
+    extra = [n for n in EXTRA_WORKLOADS if n != w.name] if not args.no_extra else []
+    side = {}
+    for name in extra:
+        wx = WORKLOADS[name]
+        r, cin, o = time_workload(dev, wx, args.steps, args.warmup, headline=False)
+        side[name] = (wx, r, cin, o)
+    if not args.no_check:
+        log(f"sampled oracle check of {w.name}")
+        rec["check"] = sampled_errors(w, cpu_in, outs)
+    for name, (wx, r, cin, o) in side.items():
+        if not args.no_check:
+            log(f"sampled oracle check of {name}")
+            r["check"] = sampled_errors(wx, cin, o)
+        rec.setdefault("workloads", {})[name] = r
+    del outs, side
+    if not args.no_cpu_baseline:
+        log("cpu oracle baseline")
+        rec["cpu_baseline"] = cpu_baseline(w, *cpu_in, args.cpu_tokens)
+    print(json.dumps(rec), flush=True)
+
+
+def time_workload(dev, w, steps, warmup, headline):
+    """Warm up, then time `steps` whole steps (fa_fwd + fa_bwd_preprocess + fa_bwd) of one
+    workload on one stream.  Returns (record, CPU inputs, outputs of the last step)."""
     code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
     B, H, S, D = w.shape
 
@@ -404,31 +524,17 @@ def main():
         check(fa.fa_bwd(qd, kd, vd, dod, lse, delta, dq, dk, dv, ws, ws_bytes, B, H, S, D,
                         w.scale, 1, code, sh), "fa_bwd")
 
-    if args.hold > 0:
-        fwd(); pre(); bwd()
-        torch.cuda.synchronize()
-        f = fwd if args.hold_entry == "fwd" else bwd
-        n, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < args.hold:
-            for _ in range(5):
-                f()
-            torch.cuda.synchronize()
-            n += 5
-        print(json.dumps({"hold_entry": args.hold_entry, "calls": n,
-                          "ms_per_call": round((time.perf_counter() - t0) * 1e3 / n, 3)}), flush=True)
-        return
-
-    log("warmup")
-    for _ in range(args.warmup):
+    log(f"warmup {w.name}")
+    for _ in range(warmup):
         fwd(); pre(); bwd()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
+    log(f"timing {steps} steps of {w.name}")
 
     # timed region: K whole steps, with per-entry-point events on the same stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         ev[i][0].record(stream)
         fwd()
         ev[i][1].record(stream)
@@ -442,10 +548,10 @@ def main():
     per_pre = [e[1].elapsed_time(e[2]) for e in ev]
     per_bwd = [e[2].elapsed_time(e[3]) for e in ev]
     per_step = [e[0].elapsed_time(e[3]) for e in ev]
-    t_fwd = sum(per_fwd) / args.steps
-    t_pre = sum(per_pre) / args.steps
-    t_bwd = sum(per_bwd) / args.steps
-    ms_step = wall * 1e3 / args.steps
+    t_fwd = sum(per_fwd) / steps
+    t_pre = sum(per_pre) / steps
+    t_bwd = sum(per_bwd) / steps
+    ms_step = wall * 1e3 / steps
 
     pairs = w.causal_pairs()
     f_fwd = 4 * D * pairs
@@ -456,21 +562,12 @@ def main():
     bwd_tf = 10 * D * pairs / (t_bwd * 1e-3) / 1e12
     esize = 2 if w.dtype == "bf16" else 4
     tensor = B * H * S * D * esize
-    rec = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    _, plan = fa.fa_get_plan(B, H, S, D, code, 0)
+    config = {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": True,
+              "scale": w.scale, "seed": w.seed, "qk_mult": w.qk_mult, "plan": plan.as_dict()}
+    timing = {
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
-        "config": {"workload": w.name, "B": B, "H": H, "S": S, "D": D, "causal": True,
-                   "scale": w.scale},
+        "fwd_bwd_tflops": round(value, 2),
         "frac_of_peak": round(value / peak, 4),
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_of_peak": round(fwd_tf / peak, 4),
@@ -487,11 +584,30 @@ def main():
                          "achieved": round(bwd_tf, 2), "peak": peak, "unit": "TFLOP/s",
                          "frac": round(bwd_tf / peak, 4)},
     }
-    log(f"gpu done: {ms_step:.3f} ms/step, {value:.1f} TFLOP/s fwd+bwd, {fwd_tf:.1f} TFLOP/s fwd")
-    if not args.no_cpu_baseline:
-        log("cpu oracle baseline")
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, do, args.cpu_tokens)
-    print(json.dumps(rec), flush=True)
+    if headline:
+        rec = {
+            "metric": METRIC,
+            "value": round(value, 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": steps,
+            "warmup": warmup,
+            "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": w.dtype,
+            "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
+            "config": config,
+        }
+        timing.pop("ms_per_step")
+        timing.pop("fwd_bwd_tflops")
+        rec.update(timing)
+    else:
+        rec = {"config": config, "steps": steps, "warmup": warmup, **timing}
+    log(f"{w.name}: {ms_step:.3f} ms/step, {value:.1f} TFLOP/s fwd+bwd, {fwd_tf:.1f} TFLOP/s fwd")
+    outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+    return rec, (q, k, v, do), outs
 
 
 if __name__ == "__main__":
