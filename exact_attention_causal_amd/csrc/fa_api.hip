@@ -109,7 +109,7 @@ size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype) {
     return fa::bwd_lse2_bytes(BH * S) + fa::bwd_part_bytes(sp, BH, S, D);
 }
 
-// Argument checks of fa_bwd.
+// Checks shared by fa_bwd and fa_bwd_noalloc.
 static int check_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                      const float *delta, void *dq, void *dk, void *dv, int B, int H, int S, int D, float scale,
                      int causal, fa_dtype dtype) {
@@ -141,6 +141,22 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const 
     const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, ncu, budget);
     return map_launch(fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv,
                                      static_cast<float *>(workspace), (int)BH, S, D, scale, causal, sp, stream));
+}
+
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+                   const float *delta, void *dq, void *dk, void *dv, int B, int H, int S, int D, float scale,
+                   int causal, fa_dtype dtype, hipStream_t stream) {
+    if (int rc = check_bwd(q, k, v, dout, lse, delta, dq, dk, dv, B, H, S, D, scale, causal, dtype)) return rc;
+    const long long BH = (long long)B * H;
+    const size_t base = fa::bwd_lse2_bytes(BH * S);
+    if (base > fa::kNoAllocScratchBytes) return FA_ESCRATCH;
+    const int ncu = fa::stream_cu_count(stream);
+    if (ncu <= 0) return FA_EHIP;
+    float *scratch = fa::noalloc_scratch(stream);
+    if (!scratch) return FA_EHIP;
+    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, ncu, fa::kNoAllocScratchBytes - base);
+    return map_launch(fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv, scratch, (int)BH, S, D,
+                                     scale, causal, sp, stream));
 }
 
 int fa_get_plan(int B, int H, int S, int D, fa_dtype dtype, int num_cu, fa_plan *plan) {
@@ -228,6 +244,7 @@ const char *fa_strerror(int status) {
     case FA_EALIGN: return "pointer not 16-byte aligned";
     case FA_EWORKSPACE: return "workspace too small";
     case FA_EHIP: return "HIP runtime error (no device visible, device query or kernel launch failed)";
+    case FA_ESCRATCH: return "problem too large for the fixed device scratch of fa_bwd_noalloc (B*H*S above 16777216)";
     default: return "unknown status";
     }
 }

@@ -24,6 +24,8 @@
 #include "fa_launch.hpp"
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 namespace fa {
 
@@ -1128,6 +1130,47 @@ int launch_bwd(int dtype, const void *q, const void *k, const void *v, const voi
                                                (bf16 *)dv, a, stream);
     return bwd_dispatch<float, float, false>(D, q, k, v, dout, lse2, delta, (float *)dq, (float *)dk,
                                              (float *)dv, a, stream);
+}
+
+// ------------------------------------------- allocation-free backward ---
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// serving loops, harnesses that forbid it), the backward can run out of a
+// fixed array in device memory instead of a caller's workspace: the base-2
+// copy of lse and, when they fit, the split's partials.  Each GPU the library
+// runs on holds its own copy until the process ends; every call on a GPU
+// shares it, so calls that overlap on one GPU race.  Nothing in it needs to
+// start at zero: every call overwrites what it reads.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// The device address of `scratch` on the device of `stream`.  In host code
+// the array's name is only a stand-in for the symbol; its address on a device
+// comes from the runtime, looked up once per device with that device current.
+float *noalloc_scratch(hipStream_t stream) {
+    int dev = -1;
+    if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    if (float *p = g_scratch[dev].load(std::memory_order_acquire)) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (float *p = g_scratch[dev].load(std::memory_order_acquire)) return p;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();  // (clear the sticky error the failed lookup left)
+        return nullptr;
+    }
+    g_scratch[dev].store(static_cast<float *>(p), std::memory_order_release);
+    return static_cast<float *>(p);
 }
 
 int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, const void *dout,

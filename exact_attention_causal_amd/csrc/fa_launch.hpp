@@ -69,6 +69,12 @@ int launch_bwd(int dtype, const void *q, const void *k, const void *v, const voi
                const float *lse, const float *delta, void *dq, void *dk, void *dv, float *lse2,
                int BH, int S, int D, float scale, int causal, BwdSplit sp, hipStream_t stream);
 
+// The allocation-free backward's device scratch (a fixed array in device
+// memory, one per GPU): its address on the device `stream` runs on, looked up
+// once per device; nullptr if the lookup failed.  kNoAllocScratchBytes is its size.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+float *noalloc_scratch(hipStream_t stream);
+
 // Gradient contributions of one key set (fp32, stored or added).
 int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, const void *dout,
                        const float *lse, const float *delta, float *dq, float *dk, float *dv,

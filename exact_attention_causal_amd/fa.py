@@ -1,7 +1,7 @@
 """ctypes binding of the gfx950 attention library (include/fa.h).
 
 The functions named like the C entry points (fa_fwd, fa_bwd_preprocess,
-fa_bwd_workspace_size, fa_bwd, fa_fwd_partial, fa_merge, fa_bwd_partial,
+fa_bwd_workspace_size, fa_bwd, fa_bwd_noalloc, fa_fwd_partial, fa_merge, fa_bwd_partial,
 fa_get_plan, fa_strerror) only marshal arguments: tensors
 become device pointers, the stream becomes HIP's stream handle, and the status
 code comes back unchanged.  ``forward`` / ``backward`` / ``attention_fwd_bwd``
@@ -28,6 +28,7 @@ FA_EUNSUPPORTED = -2
 FA_EALIGN = -3
 FA_EWORKSPACE = -4
 FA_EHIP = -5
+FA_ESCRATCH = -6
 
 #: head dimensions with built kernels
 HEAD_DIMS = (16, 32, 64, 80, 96, 128)
@@ -78,6 +79,8 @@ def load_library():
     lib.fa_merge.restype = _i
     lib.fa_bwd_partial.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _i, _i, _i, _vp]
     lib.fa_bwd_partial.restype = _i
+    lib.fa_bwd_noalloc.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.fa_bwd_noalloc.restype = _i
     lib.fa_get_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(Plan)]
     lib.fa_get_plan.restype = _i
     lib.fa_strerror.argtypes = [_i]
@@ -124,6 +127,13 @@ def fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes, B,
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                  int(workspace_bytes), B, H, S, D, float(scale), int(causal),
                                  int(dtype), _stream(stream))
+
+
+def fa_bwd_noalloc(q, k, v, dout, lse, delta, dq, dk, dv, B, H, S, D, scale, causal, dtype,
+                   stream=None):
+    return load_library().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                         _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), B, H, S, D,
+                                         float(scale), int(causal), int(dtype), _stream(stream))
 
 
 def fa_get_plan(B, H, S, D, dtype, num_cu=0):

@@ -23,15 +23,17 @@
  *
  * Ownership.  The caller allocates every buffer (including the backward
  * workspace); the library never allocates, frees, copies to or from the
- * host, or synchronises.  Outputs are fully overwritten; inputs must not
- * alias outputs.  All pointers must be device pointers aligned to 16 bytes.
+ * host, or synchronises.  (The one device memory it holds itself is the
+ * fixed scratch array of fa_bwd_noalloc, part of its code object.)  Outputs
+ * are fully overwritten; inputs must not alias outputs.  All pointers must
+ * be device pointers aligned to 16 bytes.
  *
  * Streams and errors.  All work is enqueued on `stream` (0 = the null
  * stream).  Argument errors are returned synchronously, before anything is
  * enqueued.  Faults inside a kernel surface at the caller's next stream
  * synchronisation.  Launch shapes depend on the compute-unit count of the
  * stream's device, read once per device and cached.  The library is
- * thread-safe.
+ * thread-safe, except that fa_bwd_noalloc calls on one GPU share its scratch.
  *
  * Supported shapes.  D in {16, 32, 64, 80, 96, 128}; dtype FA_F32 or FA_BF16
  * (bf16 storage, bf16 matrix-core products with fp32 accumulation; the
@@ -59,8 +61,9 @@ enum {
     FA_EUNSUPPORTED = -2, /* D or dtype not built */
     FA_EALIGN = -3,       /* a pointer is not 16-byte aligned */
     FA_EWORKSPACE = -4,   /* workspace below B*H*S fp32 values (see fa_bwd) */
-    FA_EHIP = -5          /* the HIP runtime failed: no device visible for the stream,
+    FA_EHIP = -5,         /* the HIP runtime failed: no device visible for the stream,
                              a device query failed, or a launch was refused */
+    FA_ESCRATCH = -6      /* fa_bwd_noalloc: B*H*S beyond its fixed device scratch */
 };
 
 /*
@@ -188,6 +191,25 @@ int fa_bwd_partial(const void *q, const void *k, const void *v, const void *dout
                    const float *lse, const float *delta, float *dq_acc, float *dk_acc,
                    float *dv_acc, int accumulate, int B, int H, int Sq, int Sk, int D,
                    float scale, int causal, int q_offset, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It computes what fa_bwd computes, with the same
+ * arguments minus the workspace, and allocates nothing: its scratch is a
+ * fixed 64 MiB array in device memory that the library holds on every GPU it
+ * runs on until the process ends.  It holds the base-2 lse (B*H*S fp32), so
+ * B*H*S must be at most 16777216 (FA_ESCRATCH otherwise), and the split
+ * backward's partials when they fit beside it (fewer chunks than fa_bwd with
+ * a full workspace may take; results equal up to the order of fp32 sums).
+ * Every call on one GPU uses that GPU's one array: calls that may overlap on
+ * a GPU (different streams, different threads) race and must be ordered by
+ * the caller.  No call depends on what an earlier call left in it.
+ */
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *dout,
+                   const float *lse, const float *delta, void *dq, void *dk, void *dv,
+                   int B, int H, int S, int D, float scale, int causal, fa_dtype dtype,
+                   hipStream_t stream);
 
 /*
  * The tile configuration fa_fwd and fa_bwd choose for a problem (handout,

@@ -34,7 +34,7 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_partial", "fa_bwd_preprocess",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_noalloc", "fa_bwd_partial", "fa_bwd_preprocess",
                                      "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_partial", "fa_get_plan",
                                      "fa_merge", "fa_strerror"]
 
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert fa.fa_strerror(code) and "unknown" not in fa.fa_strerror(code)
     assert fa.fa_strerror(0) == "success"
     assert "unknown" in fa.fa_strerror(17)
@@ -194,6 +194,25 @@ def test_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+def _noalloc(**kw):
+    a = dict(q=P, k=P, v=P, dout=P, lse=P, delta=P, dq=P, dk=P, dv=P, B=1, H=2, S=128, D=64,
+             scale=0.125, causal=1, dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_bwd_noalloc(**a)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), fa.FA_EINVAL), (dict(dv=None), fa.FA_EINVAL), (dict(B=0), fa.FA_EINVAL),
+    (dict(causal=2), fa.FA_EINVAL), (dict(scale=0.0), fa.FA_EINVAL),
+    (dict(D=72), fa.FA_EUNSUPPORTED), (dict(dtype=3), fa.FA_EUNSUPPORTED),
+    (dict(dq=MIS), fa.FA_EALIGN), (dict(lse=P + 4), fa.FA_EALIGN),
+    # the fixed scratch holds the base-2 lse of at most 2^24 rows
+    (dict(B=1, H=257, S=65536, D=64), fa.FA_ESCRATCH), (dict(B=2, H=1, S=(1 << 23) + 1, D=16), fa.FA_ESCRATCH),
+])
+def test_bwd_noalloc_rejects(lib, bad, code):
+    assert _noalloc(**bad) == code
 
 
 def _plan(B, H, S, D, dtype, ncu):
