@@ -173,6 +173,7 @@ int fa_get_plan(int B, int H, int S, int D, fa_dtype dtype, int num_cu, fa_plan 
     plan->fwd_block_queries = f.bq;
     plan->fwd_key_groups = f.groups;
     plan->fwd_key_tile = f.bk;
+    plan->fwd_band = f.band;
     plan->bwd_chunks = sp.n;
     plan->bwd_chunk_rows = sp.chunk;
     return FA_OK;

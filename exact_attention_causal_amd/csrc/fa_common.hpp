@@ -397,4 +397,36 @@ __device__ inline float wave_xor32_sum(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup order over the (tile, head) pairs of a launch, longest tile first
+// (rank 0 = the tile with the most work).  Workgroup i runs on XCD i % 8 (the
+// dispatcher deals workgroups to the 8 XCDs in turn; each has its own L2).
+// band = 0: consecutive workgroups take consecutive heads.  band > 0 (B*H a
+// multiple of 8): XCD x takes only heads x, x + 8, ..., in bands of `band`
+// tiles -- the band's tiles of its first head, then the same band of its next
+// head, and so on -- so the workgroups in flight on one XCD, which share its
+// L2, mostly stream the same head's tiles, while every head's longest tiles
+// still start first.  All arguments are wave-uniform.
+__device__ inline void tile_order(int bid, int BH, int ntiles, int band, int &rank, int &bh) {
+    if (band > 0) {
+        const int x = bid & 7, slot = bid >> 3, J = BH >> 3;
+        const int full = ntiles / band, per = band * J;  // full bands, slots per full band
+        int j, k;
+        if (slot < full * per) {
+            const int b = slot / per, w = slot - b * per;
+            j = w / band;
+            k = w - j * band;
+            rank = b * band + k;
+        } else {  // the last, shorter band
+            const int rem = ntiles - full * band, w = slot - full * per;
+            j = w / rem;
+            k = w - j * rem;
+            rank = full * band + k;
+        }
+        bh = x + 8 * j;
+    } else {
+        rank = bid / BH;
+        bh = bid % BH;
+    }
+}
+
 }  // namespace fa

@@ -21,11 +21,16 @@ inline bool head_dim_supported(int D) {
 // argument.
 int stream_cu_count(hipStream_t stream);
 
+// XCDs of the GPU: workgroup i of a launch runs on XCD i % kNumXcd (the
+// dispatcher deals workgroups to the XCDs in turn; each has its own L2).
+constexpr int kNumXcd = 8;
+
 // Forward tile configuration of a self-attention problem: queries per
 // workgroup, key groups per workgroup (2: two wave groups split the key tiles
-// and merge) and keys per LDS tile.
+// and merge), keys per LDS tile, and the workgroup order (band: see
+// tile_order; 0 = consecutive workgroups take consecutive heads).
 struct FwdPlan {
-    int bq, groups, bk;
+    int bq, groups, bk, band;
 };
 FwdPlan fwd_plan(int dtype, int BH, int S, int D, int ncu);
 

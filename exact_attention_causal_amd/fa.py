@@ -43,6 +43,7 @@ class Plan(ctypes.Structure):
     """fa_plan: the tile configuration the library picks for a problem (include/fa.h)."""
     _fields_ = [("num_cu", ctypes.c_int), ("fwd_block_queries", ctypes.c_int),
                 ("fwd_key_groups", ctypes.c_int), ("fwd_key_tile", ctypes.c_int),
+                ("fwd_band", ctypes.c_int),
                 ("bwd_chunks", ctypes.c_int), ("bwd_chunk_rows", ctypes.c_int)]
 
     def as_dict(self):

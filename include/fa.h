@@ -222,6 +222,10 @@ typedef struct {
     int fwd_block_queries;  /* queries per forward workgroup: 128, 256 or 512 */
     int fwd_key_groups;     /* 2: two wave groups split the key tiles and merge; else 1 */
     int fwd_key_tile;       /* keys per LDS tile of the forward */
+    int fwd_band;           /* forward workgroup order: 0 = consecutive workgroups take
+                               consecutive heads; b > 0 = each of the 8 XCDs takes every
+                               8th head, in bands of b query tiles per head (B*H a
+                               multiple of 8) */
     int bwd_chunks;         /* chunks of the split backward (1: not split), with a
                                workspace of fa_bwd_workspace_size() bytes */
     int bwd_chunk_rows;     /* rows per chunk (S when not split) */

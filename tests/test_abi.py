@@ -228,7 +228,10 @@ def test_plan_thresholds_follow_the_cu_count(lib):
     # S=65536, D=128, 16 heads: 2048 tiles of 512 queries = 8 per CU on 256 CUs (64 queries per
     # wave); below 4 per CU (1024 CUs) the 256-query tile; at 1.5 tiles of 256 per CU or fewer
     # (3072 CUs and up) two key groups on 128-query tiles
-    assert (_plan(1, 16, 65536, 128, bf, 256).fwd_block_queries, _plan(1, 16, 65536, 128, bf, 256).fwd_key_tile) == (512, 32)
+    p = _plan(1, 16, 65536, 128, bf, 256)
+    assert (p.fwd_block_queries, p.fwd_key_tile, p.fwd_band) == (512, 32, 64)   # 16 heads: banded order
+    assert _plan(1, 12, 65536, 128, bf, 256).fwd_band == 0    # 12 heads do not split over 8 XCDs
+    assert _plan(1, 32, 16000, 80, bf, 256).fwd_band == 0     # D = 80: consecutive heads
     assert _plan(1, 16, 65536, 128, bf, 512).fwd_block_queries == 512    # exactly 4 per CU
     assert _plan(1, 16, 65536, 128, bf, 513).fwd_block_queries == 256
     assert _plan(1, 16, 65536, 128, bf, 2730).fwd_key_groups == 1        # 4096 > 1.5 * 2730

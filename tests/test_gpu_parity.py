@@ -695,3 +695,47 @@ def test_forward_on_a_side_stream():
         o, _ = fa.forward(qd, kd, vd, stream=s)
     s.synchronize()
     assert torch.equal(o, ref)
+
+
+# ------------------------------------------- workgroup order of the forward ---
+
+def _banded_forward(B, H, S, heads, rows=None):
+    """Forward through a launch that takes the banded XCD order (the 512-query D=128 tile,
+    B*H a multiple of 8); outputs start as NaN so a (head, tile) the order skipped shows."""
+    D = 128
+    rc, plan = fa.fa_get_plan(B, H, S, D, fa.FA_BF16, 0)
+    assert rc == 0 and plan.fwd_block_queries == 512 and plan.fwd_band > 0, plan.as_dict()
+    print(f"[parity] banded forward B={B} H={H} S={S} band={plan.fwd_band}", flush=True)
+    q, k, v, do = make_inputs(B, H, S, D, "bf16", seed=900 + H)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, H, S), float("nan"), device=dev)
+    fa.forward(qd, kd, vd, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    on = o.double().cpu().numpy().reshape(B * H, S, D)
+    ln = lse.double().cpu().numpy().reshape(B * H, S)
+    qn, kn, vn, don = (x.double().numpy().reshape(B * H, S, D) for x in (q, k, v, do))
+    ro, rl, go, gl = [], [], [], []
+    for hh in heads:
+        rr = list(range(S)) if rows is None else rows
+        o_ref, l_ref, _ = oracle.rows(qn[hh], kn[hh], vn[hh], don[hh], rr)
+        ro.append(o_ref); rl.append(l_ref); go.append(on[hh][rr]); gl.append(ln[hh][rr])
+    eo = rel(np.concatenate(go), np.concatenate(ro))
+    el = absdiff(np.concatenate(gl), np.concatenate(rl))
+    print(f"[parity] banded forward errors o={eo:.3e} lse={el:.3e}", flush=True)
+    assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+
+
+def test_banded_order_partial_bands():
+    # 1024 heads of 3 query tiles: every XCD's heads fall in one partial band
+    _banded_forward(2, 512, 1100, heads=[0, 1, 7, 8, 9, 513, 1016, 1023])
+
+
+@pytest.mark.slow
+def test_banded_order_full_bands_and_remainder():
+    # 8 heads of 129 query tiles: two full bands of 64 and a one-tile remainder per head
+    S = 64 * 1024 + 300
+    rows = [0, 1, 511, 512, 32767, 32768, 65535, 65536, S - 300, S - 2, S - 1]
+    _banded_forward(1, 8, S, heads=[0, 3, 7], rows=rows)
