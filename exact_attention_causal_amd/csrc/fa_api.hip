@@ -75,7 +75,7 @@ int map_launch(int rc) {
 extern "C" {
 
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S,
-           int D, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+           int D, float scale, int causal, int dtype, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return FA_EINVAL;
     if (causal != 0 && causal != 1) return FA_EINVAL;
     if (int rc = check_scale(scale)) return rc;
@@ -91,14 +91,14 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
 }
 
 int fa_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int S, int D,
-                      fa_dtype dtype, hipStream_t stream) {
+                      int dtype, hipStream_t stream) {
     if (!o || !dout || !delta) return FA_EINVAL;
     if (int rc = check_shape(B, H, S, D, dtype)) return rc;
     if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return FA_EALIGN;
     return map_launch(fa::launch_delta(dtype, o, dout, delta, B * H, S, D, stream));
 }
 
-size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype) {
+size_t fa_bwd_workspace_size(int B, int H, int S, int D, int dtype) {
     if (check_shape(B, H, S, D, dtype) != FA_OK) return 0;
     const long long BH = (long long)B * H;
     // bf16 problems with few key tiles per CU: fp32 partial dQ, dK, dV of
@@ -112,7 +112,7 @@ size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype) {
 // Checks shared by fa_bwd and fa_bwd_noalloc.
 static int check_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                      const float *delta, void *dq, void *dk, void *dv, int B, int H, int S, int D, float scale,
-                     int causal, fa_dtype dtype) {
+                     int causal, int dtype) {
     if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv) return FA_EINVAL;
     if (causal != 0 && causal != 1) return FA_EINVAL;
     if (int rc = check_scale(scale)) return rc;
@@ -127,7 +127,7 @@ static int check_bwd(const void *q, const void *k, const void *v, const void *do
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
            const float *delta, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
-           int B, int H, int S, int D, float scale, int causal, fa_dtype dtype, hipStream_t stream) {
+           int B, int H, int S, int D, float scale, int causal, int dtype, hipStream_t stream) {
     if (int rc = check_bwd(q, k, v, dout, lse, delta, dq, dk, dv, B, H, S, D, scale, causal, dtype)) return rc;
     if (!workspace) return FA_EINVAL;
     if (!aligned16(workspace)) return FA_EALIGN;
@@ -145,7 +145,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const 
 
 int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                    const float *delta, void *dq, void *dk, void *dv, int B, int H, int S, int D, float scale,
-                   int causal, fa_dtype dtype, hipStream_t stream) {
+                   int causal, int dtype, hipStream_t stream) {
     if (int rc = check_bwd(q, k, v, dout, lse, delta, dq, dk, dv, B, H, S, D, scale, causal, dtype)) return rc;
     const long long BH = (long long)B * H;
     const size_t base = fa::bwd_lse2_bytes(BH * S);
@@ -159,7 +159,7 @@ int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *dout
                                      scale, causal, sp, stream));
 }
 
-int fa_get_plan(int B, int H, int S, int D, fa_dtype dtype, int num_cu, fa_plan *plan) {
+int fa_get_plan(int B, int H, int S, int D, int dtype, int num_cu, fa_plan *plan) {
     if (!plan) return FA_EINVAL;
     if (int rc = check_shape(B, H, S, D, dtype)) return rc;
     if (num_cu <= 0) {
@@ -181,7 +181,7 @@ int fa_get_plan(int B, int H, int S, int D, fa_dtype dtype, int num_cu, fa_plan 
 
 int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, float *lse_parts,
                    int B, int H, int Sq, int Sk, int D, float scale, int causal, int q_offset,
-                   int n_split, fa_dtype dtype, hipStream_t stream) {
+                   int n_split, int dtype, hipStream_t stream) {
     if (!q || !k || !v || !o_parts || !lse_parts) return FA_EINVAL;
     if (causal != 0 && causal != 1) return FA_EINVAL;
     if (n_split < 1 || n_split > 65535) return FA_EINVAL;
@@ -205,7 +205,7 @@ int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, 
 }
 
 int fa_merge(const float *o_parts, const float *lse_parts, int n_parts, void *o, float *lse, int B,
-             int H, int S, int D, fa_dtype dtype, hipStream_t stream) {
+             int H, int S, int D, int dtype, hipStream_t stream) {
     if (!o_parts || !lse_parts || !o || !lse) return FA_EINVAL;
     if (n_parts < 1) return FA_EINVAL;
     if (int rc = check_shape(B, H, S, D, dtype)) return rc;
@@ -218,7 +218,7 @@ int fa_merge(const float *o_parts, const float *lse_parts, int n_parts, void *o,
 
 int fa_bwd_partial(const void *q, const void *k, const void *v, const void *dout, const float *lse,
                    const float *delta, float *dq_acc, float *dk_acc, float *dv_acc, int accumulate, int B,
-                   int H, int Sq, int Sk, int D, float scale, int causal, int q_offset, fa_dtype dtype,
+                   int H, int Sq, int Sk, int D, float scale, int causal, int q_offset, int dtype,
                    hipStream_t stream) {
     if (!q || !k || !v || !dout || !lse || !delta || !dq_acc || !dk_acc || !dv_acc) return FA_EINVAL;
     if (causal != 0 && causal != 1) return FA_EINVAL;

@@ -18,7 +18,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
+# FA_LIB_PATH selects another build of the library (the host-sanitized build of
+# build_sanitized.py, loaded with the sanitizer runtime preloaded)
+LIB_PATH = os.environ.get("FA_LIB_PATH") or os.path.join(HERE, "libfa_mi355x.so")
 
 FA_F32 = 0
 FA_BF16 = 1

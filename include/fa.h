@@ -52,6 +52,8 @@ extern "C" {
 /* HIP's stream handle (identical to the typedef in hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
+/* Element type codes, passed to the entry points as an int `dtype`: any other
+ * value returns FA_EUNSUPPORTED. */
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 
 /* Status codes: 0 = success; negative = error, and nothing was enqueued. */
@@ -74,7 +76,7 @@ enum {
  * Tiles of keys that lie wholly above the diagonal are never visited.
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
-           int B, int H, int S, int D, float scale, int causal, fa_dtype dtype,
+           int B, int H, int S, int D, float scale, int causal, int dtype,
            hipStream_t stream);
 
 /*
@@ -84,7 +86,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *   o, dout : [B][H][S][D] inputs          delta : [B][H][S] fp32 output
  */
 int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
-                      int B, int H, int S, int D, fa_dtype dtype, hipStream_t stream);
+                      int B, int H, int S, int D, int dtype, hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: B*H*S fp32 values
@@ -99,7 +101,7 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
  * current device's (that of one MI355X, 256, when no device is visible).
  * Returns 0 for invalid sizes; fa_bwd reports those.
  */
-size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
+size_t fa_bwd_workspace_size(int B, int H, int S, int D, int dtype);
 
 /*
  * Backward pass (handout section 4.2.3, Algorithm 2; Eq. 13-19), with the
@@ -121,7 +123,7 @@ size_t fa_bwd_workspace_size(int B, int H, int S, int D, fa_dtype dtype);
 int fa_bwd(const void *q, const void *k, const void *v, const void *dout,
            const float *lse, const float *delta, void *dq, void *dk, void *dv,
            void *workspace, size_t workspace_bytes,
-           int B, int H, int S, int D, float scale, int causal, fa_dtype dtype,
+           int B, int H, int S, int D, float scale, int causal, int dtype,
            hipStream_t stream);
 
 /*
@@ -148,7 +150,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout,
  */
 int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, float *lse_parts,
                    int B, int H, int Sq, int Sk, int D, float scale, int causal, int q_offset,
-                   int n_split, fa_dtype dtype, hipStream_t stream);
+                   int n_split, int dtype, hipStream_t stream);
 
 /*
  * Merge n_parts results over disjoint key sets of the same queries (the same
@@ -163,7 +165,7 @@ int fa_fwd_partial(const void *q, const void *k, const void *v, float *o_parts, 
  * dtype as fa_fwd.
  */
 int fa_merge(const float *o_parts, const float *lse_parts, int n_parts, void *o, float *lse,
-             int B, int H, int S, int D, fa_dtype dtype, hipStream_t stream);
+             int B, int H, int S, int D, int dtype, hipStream_t stream);
 
 /*
  * Gradient contributions of one key set, for attention split over keys (the
@@ -190,7 +192,7 @@ int fa_merge(const float *o_parts, const float *lse_parts, int n_parts, void *o,
 int fa_bwd_partial(const void *q, const void *k, const void *v, const void *dout,
                    const float *lse, const float *delta, float *dq_acc, float *dk_acc,
                    float *dv_acc, int accumulate, int B, int H, int Sq, int Sk, int D,
-                   float scale, int causal, int q_offset, fa_dtype dtype, hipStream_t stream);
+                   float scale, int causal, int q_offset, int dtype, hipStream_t stream);
 
 /*
  * fa_bwd without a workspace argument, for callers that cannot allocate
@@ -208,7 +210,7 @@ int fa_bwd_partial(const void *q, const void *k, const void *v, const void *dout
  */
 int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *dout,
                    const float *lse, const float *delta, void *dq, void *dk, void *dv,
-                   int B, int H, int S, int D, float scale, int causal, fa_dtype dtype,
+                   int B, int H, int S, int D, float scale, int causal, int dtype,
                    hipStream_t stream);
 
 /*
@@ -231,7 +233,7 @@ typedef struct {
     int bwd_chunk_rows;     /* rows per chunk (S when not split) */
 } fa_plan;
 
-int fa_get_plan(int B, int H, int S, int D, fa_dtype dtype, int num_cu, fa_plan *plan);
+int fa_get_plan(int B, int H, int S, int D, int dtype, int num_cu, fa_plan *plan);
 
 /* Static, human-readable text for a status code. */
 const char *fa_strerror(int status);

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB selects another build of the same source (the sanitizer build of
+# oracle/build.py --sanitize, run with the sanitizer runtimes preloaded)
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
