@@ -615,6 +615,31 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
 #pragma unroll
                 for (int st = 0; st < C::NSD; ++st) s = M::run(qa[st], bk[st], s);
             }
+            // D - dP (Eq. 16).  Up to D = 96 its products are issued before the
+            // exponentials, which then run while they execute (0.7 % faster at
+            // D = 80); at D = 128 holding S and dP together spills.
+            f32x16 dp;
+            auto form_dp = [&]() {
+                {
+                    float dl[16];
+                    stat(dl, tdO, qb, 1.f);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dp[r] = dl[r];
+                    frag da[C::NSD];
+                    load_row_frags<T, D>(da, tdO, 32 * qb + rsigma(l32), h);
+                    if constexpr (C::VLDS) {
+                        frag bvl[C::VL];
+                        load_run<T, C::VL>(bvl, sVl);
+#pragma unroll
+                        for (int st = 0; st < C::NSD; ++st)
+                            dp = M::run(da[st], st < C::VREG ? bv[st < C::VREG ? st : 0] : bvl[st < C::VREG ? 0 : st - C::VREG], dp);
+                    } else {
+#pragma unroll
+                        for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bv[st], dp);
+                    }
+                }
+            };
+            if constexpr (C::D <= 96) form_dp();
             {
                 float lv[16];
                 stat(lv, tQ, qb, GEN ? kLog2e : 1.f);  // (self-attention: already base 2)
@@ -652,26 +677,8 @@ __global__ __launch_bounds__(C::NT) void dkdv1_kernel(const T *__restrict__ q, c
                     tailV[1] = mma16(ta, b1, tailV[1]);
                 }
             }
-            // D - dP (Eq. 16), then -dS = P o (D - dP) (Eq. 17)
-            f32x16 dp;
-            {
-                float dl[16];
-                stat(dl, tdO, qb, 1.f);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dp[r] = dl[r];
-                frag da[C::NSD];
-                load_row_frags<T, D>(da, tdO, 32 * qb + rsigma(l32), h);
-                if constexpr (C::VLDS) {
-                    frag bvl[C::VL];
-                    load_run<T, C::VL>(bvl, sVl);
-#pragma unroll
-                    for (int st = 0; st < C::NSD; ++st)
-                        dp = M::run(da[st], st < C::VREG ? bv[st < C::VREG ? st : 0] : bvl[st < C::VREG ? 0 : st - C::VREG], dp);
-                } else {
-#pragma unroll
-                    for (int st = 0; st < C::NSD; ++st) dp = M::run(da[st], bv[st], dp);
-                }
-            }
+            if constexpr (C::D > 96) form_dp();
+            // -dS = P o (D - dP) (Eq. 17)
 #pragma unroll
             for (int r = 0; r < 16; ++r) dp[r] *= s[r];
             // -dK^T += Q^T (-dS) (Eq. 19)

@@ -699,19 +699,19 @@ def test_forward_on_a_side_stream():
 
 # ------------------------------------------- workgroup order of the forward ---
 
-def _banded_forward(B, H, S, heads, rows=None):
+def _banded_forward(B, H, S, heads, rows=None, causal=True):
     """Forward through a launch that takes the banded XCD order (the 512-query D=128 tile,
     B*H a multiple of 8); outputs start as NaN so a (head, tile) the order skipped shows."""
     D = 128
     rc, plan = fa.fa_get_plan(B, H, S, D, fa.FA_BF16, 0)
     assert rc == 0 and plan.fwd_block_queries == 512 and plan.fwd_band > 0, plan.as_dict()
-    print(f"[parity] banded forward B={B} H={H} S={S} band={plan.fwd_band}", flush=True)
+    print(f"[parity] banded forward B={B} H={H} S={S} band={plan.fwd_band} causal={causal}", flush=True)
     q, k, v, do = make_inputs(B, H, S, D, "bf16", seed=900 + H)
     dev = torch.device("cuda:0")
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
     o = torch.full_like(qd, float("nan"))
     lse = torch.full((B, H, S), float("nan"), device=dev)
-    fa.forward(qd, kd, vd, causal=True, out=o, lse=lse)
+    fa.forward(qd, kd, vd, causal=causal, out=o, lse=lse)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     on = o.double().cpu().numpy().reshape(B * H, S, D)
@@ -720,7 +720,7 @@ def _banded_forward(B, H, S, heads, rows=None):
     ro, rl, go, gl = [], [], [], []
     for hh in heads:
         rr = list(range(S)) if rows is None else rows
-        o_ref, l_ref, _ = oracle.rows(qn[hh], kn[hh], vn[hh], don[hh], rr)
+        o_ref, l_ref, _ = oracle.rows(qn[hh], kn[hh], vn[hh], don[hh], rr, causal=causal)
         ro.append(o_ref); rl.append(l_ref); go.append(on[hh][rr]); gl.append(ln[hh][rr])
     eo = rel(np.concatenate(go), np.concatenate(ro))
     el = absdiff(np.concatenate(gl), np.concatenate(rl))
@@ -728,9 +728,10 @@ def _banded_forward(B, H, S, heads, rows=None):
     assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
 
 
-def test_banded_order_partial_bands():
+@pytest.mark.parametrize("causal", [True, False])
+def test_banded_order_partial_bands(causal):
     # 1024 heads of 3 query tiles: every XCD's heads fall in one partial band
-    _banded_forward(2, 512, 1100, heads=[0, 1, 7, 8, 9, 513, 1016, 1023])
+    _banded_forward(2, 512, 1100, heads=[0, 1, 7, 8, 9, 513, 1016, 1023], causal=causal)
 
 
 @pytest.mark.slow
