@@ -860,6 +860,10 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
     // replicate builds: D = 16 and 32 -1.8 %, D = 64 -1.6 %, D = 96 -1.0 %;
     // D = 80 measured 0.3 % slower and keeps one block at a time.
     constexpr bool kPhased = C::KPL == 8 && C::D <= 96 && C::D != 80 && NQB == 1;
+    // bf16 D = 128 (no registers for two score blocks and two dP blocks): only
+    // block 1's S^T goes out early.  Backward 1.0-1.3 % faster at S = 65536 and
+    // 0.3 % at S = 16384 (replicate builds, interleaved); 0.7 % slower at D = 80.
+    constexpr bool kHalfPhased = C::KPL == 8 && C::D == 128 && NQB == 1 && C::NKB == 2;
 
     auto step = [&](const T *tK, const T *tV, T *nK, T *nV, int j) {
         const int j0 = j * BK;
@@ -932,6 +936,69 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
                     tacc[0][1] = mma16(ta, b1, tacc[0][1]);
                 }
             }
+        } else if constexpr (kHalfPhased) {
+            // Block 1's S^T products go out before block 0's exponentials, -dS^T
+            // and dQ^T products (and its dP^T products after them), so those run
+            // while block 1's scores are formed; holds one more score block.
+            const bool need_mask = (causal && j0 + BK - 1 > qw0 + off) || (j0 + BK > Sk);
+            const int qi = qw0 + l32;
+            f32x16 s[2], dp[2];
+            auto s_prod = [&](int kb) {
+                s[kb] = f32x16{};
+                frag ka[C::NSD];
+                load_row_frags<T, D>(ka, tK, kb * 32 + rsigma(l32), h);
+#pragma unroll
+                for (int st = 0; st < C::NSD; ++st) s[kb] = M::run(ka[st], qf[0][st], s[kb]);
+            };
+            auto dp_prod = [&](int kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dp[kb][r] = dl[0];
+                frag va[C::NSD];
+                load_row_frags<T, D>(va, tV, kb * 32 + rsigma(l32), h);
+#pragma unroll
+                for (int st = 0; st < C::NSD; ++st) dp[kb] = M::run(va[st], df[0][st], dp[kb]);
+            };
+            auto rest = [&](int kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(fmaf(s[kb][r], c, -lq[0]));  // Eq. 14
+                if (need_mask) {
+                    asm volatile("");  // a real branch: only diagonal / tail tiles pay for masking
+                    const int t = (causal ? min(qi + 1 + off, Sk) : Sk) - j0 - 32 * kb - 2 * h;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] = (ridx(r, 0) < t) ? s[kb][r] : 0.f;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dp[kb][r] = s[kb][r] * dp[kb][r];  // -dS^T (Eq. 17)
+                frag sf[C::NI];
+                to_bfrag<T>(sf, dp[kb]);
+#pragma unroll
+                for (int db = 0; db < C::ND; ++db) {
+                    frag a[C::NI];
+                    tr.load(a, tK, kb, db);
+#pragma unroll
+                    for (int i = 0; i < C::NI; ++i) acc[0][db] = M::run(a[i], sf[i], acc[0][db]);  // Eq. 18
+                }
+                if constexpr (C::TAIL) {
+                    bf16x8 b0, b1;
+                    tail_bfrag(sf, b0, b1);
+                    const bf16x8 ta = tt.load(tK, kb, 32 * C::ND);
+                    tacc[0][0] = mma16(ta, b0, tacc[0][0]);
+                    tacc[0][1] = mma16(ta, b1, tacc[0][1]);
+                }
+            };
+            static_assert(C::NKB == 2, "two key blocks per tile");
+            __builtin_amdgcn_sched_barrier(0);
+            dma.issue_part(0, C::NKB, nT, rs, hw);
+            s_prod(0);
+            __builtin_amdgcn_sched_barrier(0);
+            dp_prod(0);
+            __builtin_amdgcn_sched_barrier(0);
+            dma.issue_part(1, C::NKB, nT, rs, hw);
+            s_prod(1);
+            rest(0);
+            __builtin_amdgcn_sched_barrier(0);
+            dp_prod(1);
+            rest(1);
         } else {
             const bool need_mask = (causal && j0 + BK - 1 > qw0 + off) || (j0 + BK > Sk);
 #pragma unroll
