@@ -38,10 +38,13 @@ EXTRA_WORKLOADS = ("bf16_b1h32_s16000_d80",)
 
 # HBM traffic of one forward-kernel launch on the default workload, from two
 # rocprofv3 --pmc passes (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a
-# plain 1 GiB copy calibrates; see profiles/), keyed by a hash of the forward
-# kernel's sources: once those change, the figure is stale and reported as null.
-FWD_TRAFFIC = {"sources_sha1": "70b9e8d3cfc902e2d062537e758cff9f7cbf548d", "bytes": 9507919552}
-FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp")
+# plain 1 GiB copy calibrates; profiles/attn_bf16_b1h16_s65536_d128.md), keyed
+# by a hash of every source the forward kernel and its launch plan compile
+# from: once one changes, the figure is stale and reported as null until the
+# counters are taken again.
+FWD_TRAFFIC = {"sources_sha1": "6e1bb18a053edd94c734b10ccabad4123b246a33", "bytes": 4668701952}
+FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp",
+               "exact_attention_causal_amd/csrc/fa_launch.hpp")
 
 
 def fwd_sources_sha1():
