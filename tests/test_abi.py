@@ -263,3 +263,37 @@ def test_plan_rejects(lib):
     assert fa.fa_get_plan(1, 1, 0, 64, fa.FA_BF16, 256)[0] == fa.FA_EINVAL
     assert fa.fa_get_plan(1, 1, 128, 72, fa.FA_BF16, 256)[0] == fa.FA_EUNSUPPORTED
     assert fa.load_library().fa_get_plan(1, 1, 128, 64, 1, 256, None) == fa.FA_EINVAL
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/fa.h declares a C ABI: a C99 translation unit that calls every entry point
+    compiles against it (and so does C++)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(r'''
+#include "fa.h"
+int use(void *p, hipStream_t st) {
+    fa_plan plan;
+    int rc = fa_get_plan(1, 2, 128, 64, FA_BF16, 256, &plan);
+    rc |= fa_fwd(p, p, p, p, (float *)p, 1, 2, 128, 64, 0.125f, 1, FA_BF16, st);
+    rc |= fa_bwd_preprocess(p, p, (float *)p, 1, 2, 128, 64, FA_BF16, st);
+    size_t ws = fa_bwd_workspace_size(1, 2, 128, 64, FA_BF16);
+    rc |= fa_bwd(p, p, p, p, (const float *)p, (const float *)p, p, p, p, p, ws, 1, 2, 128, 64, 0.125f, 1,
+                 FA_BF16, st);
+    rc |= fa_bwd_noalloc(p, p, p, p, (const float *)p, (const float *)p, p, p, p, 1, 2, 128, 64, 0.125f, 1,
+                         FA_F32, st);
+    rc |= fa_fwd_partial(p, p, p, (float *)p, (float *)p, 1, 2, 128, 256, 64, 0.125f, 1, 128, 2, FA_BF16, st);
+    rc |= fa_merge((const float *)p, (const float *)p, 2, p, (float *)p, 1, 2, 128, 64, FA_BF16, st);
+    rc |= fa_bwd_partial(p, p, p, p, (const float *)p, (const float *)p, (float *)p, (float *)p, (float *)p, 0,
+                         1, 2, 128, 256, 64, 0.125f, 1, 128, FA_BF16, st);
+    return rc + (fa_strerror(rc) != 0) + plan.num_cu;
+}
+''')
+    for lang, std in (("c", "-std=c99"), ("c++", "-std=c++17")):
+        r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+                            "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
