@@ -740,3 +740,41 @@ def test_banded_order_full_bands_and_remainder():
     S = 64 * 1024 + 300
     rows = [0, 1, 511, 512, 32767, 32768, 65535, 65536, S - 300, S - 2, S - 1]
     _banded_forward(1, 8, S, heads=[0, 3, 7], rows=rows)
+
+
+# ------------------------------------------------ tile selection on the device ---
+
+def test_plan_uses_the_device_cu_count():
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    rc, plan = fa.fa_get_plan(1, 16, 65536, 128, fa.FA_BF16, 0)
+    assert rc == 0 and plan.num_cu == n, (rc, plan.as_dict(), n)
+    rc2, explicit = fa.fa_get_plan(1, 16, 65536, 128, fa.FA_BF16, n)
+    assert rc2 == 0 and explicit.as_dict() == plan.as_dict()
+
+
+def test_backward_with_a_partial_split_workspace():
+    """A workspace that holds the partials of fewer chunks than fa_bwd_workspace_size asks for
+    takes as many chunks as fit; the gradients still match the oracle."""
+    B, H, S, D = 1, 1, 4096, 128
+    rc, plan = fa.fa_get_plan(B, H, S, D, fa.FA_BF16, 0)
+    assert rc == 0 and plan.bwd_chunks >= 4, plan.as_dict()
+    q, k, v, do = make_inputs(B, H, S, D, "bf16", seed=811)
+    r = oracle.backward(*(x.double().numpy() for x in (q, k, v, do)), causal=True)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=True)
+    base = (B * H * S * 4 + 255) // 256 * 256
+    per_chunk = 3 * B * H * S * D * 4
+    outs = {}
+    for chunks in (plan.bwd_chunks, 3, 2, 1):
+        print(f"[parity] split backward with a workspace for {chunks} chunk(s)", flush=True)
+        ws = torch.empty(base + (per_chunk * chunks if chunks > 1 else 0), device=dev, dtype=torch.uint8)
+        dq, dk, dv, _ = fa.backward(qd, kd, vd, o, lse, dod, causal=True, workspace=ws)
+        torch.cuda.synchronize()
+        g = {n: t.double().cpu().numpy() for n, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+        for n in g:
+            assert rel(g[n], r[n]) <= TOL["bf16"]["grad"], (chunks, n, rel(g[n], r[n]))
+        outs[chunks] = g
+    # different chunk counts sum the same contributions in a different order
+    for n in ("dq", "dk", "dv"):
+        assert rel(outs[2][n], outs[1][n]) <= 1e-2
