@@ -36,13 +36,14 @@ DEFAULT_WORKLOAD = "bf16_b1h16_s65536_d128"
 # the other workload with a throughput target (S >= 16k), timed beside the headline one
 EXTRA_WORKLOADS = ("bf16_b1h32_s16000_d80",)
 
-# HBM traffic of one forward-kernel launch on the default workload, from two
+# HBM traffic of one forward-kernel launch on each long workload, from two
 # rocprofv3 --pmc passes (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a
-# plain 1 GiB copy calibrates; profiles/attn_bf16_b1h16_s65536_d128.md), keyed
+# plain 1 GiB copy calibrates; profiles/attn_bf16_*.md), keyed
 # by a hash of every source the forward kernel and its launch plan compile
 # from: once one changes, the figure is stale and reported as null until the
 # counters are taken again.
-FWD_TRAFFIC = {"sources_sha1": "6e1bb18a053edd94c734b10ccabad4123b246a33", "bytes": 4668701952}
+FWD_TRAFFIC = {"sources_sha1": "6e1bb18a053edd94c734b10ccabad4123b246a33",
+               "bytes": {"bf16_b1h16_s65536_d128": 4668701952, "bf16_b1h32_s16000_d80": 2120593792}}
 FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp",
                "exact_attention_causal_amd/csrc/fa_launch.hpp")
 
@@ -580,8 +581,8 @@ def time_workload(dev, w, steps, warmup, headline):
                            for n, x in (("step", per_step), ("fwd", per_fwd), ("bwd", per_bwd))},
         "roofline": {"kernel": "fwd_kernel (fa_fwd)", "bound": "mfma", "achieved": round(fwd_tf, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tf / peak, 4),
-                     "traffic": (FWD_TRAFFIC["bytes"] if w.name == DEFAULT_WORKLOAD
-                                 and FWD_TRAFFIC["sources_sha1"] == fwd_sources_sha1() else None),
+                     "traffic": (FWD_TRAFFIC["bytes"].get(w.name)
+                                 if FWD_TRAFFIC["sources_sha1"] == fwd_sources_sha1() else None),
                      "algorithmic_per_launch": {"flop": f_fwd, "bytes": 4 * tensor + 4 * B * H * S}},
         "roofline_bwd": {"kernel": "dK/dV + dQ kernels (fa_bwd)", "bound": "mfma",
                          "achieved": round(bwd_tf, 2), "peak": peak, "unit": "TFLOP/s",
