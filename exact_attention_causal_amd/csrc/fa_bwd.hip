@@ -1333,16 +1333,24 @@ int launch_bwd_partial(int dtype, const void *q, const void *k, const void *v, c
 // Every kernel the dispatch above can launch, instantiated explicitly (the
 // host compilation pass has been seen to drop the launch stubs of some
 // implicitly instantiated kernel templates).
+// (dK/dV: the one-wave kernel for bf16, the pair kernel for fp32; see kv_single)
 #define FA_BWD_KERNELS(T, D, OUT, GEN)                                                                       \
-    template __global__ void dkdv_kernel<T, KvTileFor<T, D>, OUT, GEN>(                                     \
-        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, OUT *, BwdShape);  \
     template __global__ void dq_kernel<T, QTileFor<T, D>, OUT, GEN>(                                        \
-        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, BwdShape);  \
+        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, BwdShape);
+#define FA_BWD_KV1(T, D, OUT, GEN)                                                                           \
     template __global__ void dkdv1_kernel<T, KvTile1For<T, D>, OUT, GEN>(                                   \
         const T *, const T *, const T *, const T *, const float *, const float *, OUT *, OUT *, BwdShape);
-#define FA_BWD_HEAD(T, D)                 \
-    FA_BWD_KERNELS(T, D, T, false)        \
-    FA_BWD_KERNELS(T, D, float, true)
+#define FA_BWD_KV2(T, D, OUT, GEN)                                                                           \
+    template __global__ void dkdv_kernel<T, KvTileFor<T, D>, OUT, GEN>(                                     \
+        const T *, const T *, const T *, const T *, const float *, const float *, OUT *, OUT *, BwdShape);
+#define FA_BWD_HEAD(T, D)                                                                   \
+    static_assert(kv_single<T, D>() == (sizeof(T) == 2), "dK/dV kernel instantiated below"); \
+    FA_BWD_KERNELS(T, D, T, false)                                                          \
+    FA_BWD_KERNELS(T, D, float, true)                                                       \
+    FA_BWD_KV_FOR_##T(T, D, T, false)                                                       \
+    FA_BWD_KV_FOR_##T(T, D, float, true)
+#define FA_BWD_KV_FOR_bf16 FA_BWD_KV1
+#define FA_BWD_KV_FOR_float FA_BWD_KV2
 FA_BWD_HEAD(bf16, 16)
 FA_BWD_HEAD(bf16, 32)
 FA_BWD_HEAD(bf16, 64)
@@ -1356,6 +1364,10 @@ FA_BWD_HEAD(float, 80)
 FA_BWD_HEAD(float, 96)
 FA_BWD_HEAD(float, 128)
 #undef FA_BWD_HEAD
+#undef FA_BWD_KV_FOR_bf16
+#undef FA_BWD_KV_FOR_float
+#undef FA_BWD_KV2
+#undef FA_BWD_KV1
 #undef FA_BWD_KERNELS
 
 }  // namespace fa
