@@ -88,6 +88,10 @@ def parse():
                     help="only time the benchmark sweep (B=1, H=1, S = 128 .. 65536 in powers of "
                          "two, D in 16/32/64/128, bf16 and fp32, causal and not), print a "
                          "markdown table and exit")
+    ap.add_argument("--graph", action="store_true",
+                    help="only time whole fwd+bwd steps launched one call at a time against the "
+                         "same step captured once as a HIP graph and replayed, on the small "
+                         "workloads and one-head shapes; print a markdown table and exit")
     return ap.parse_args()
 
 
@@ -368,6 +372,70 @@ def sweep(dev):
     return rows
 
 
+def graph_steps(dev):
+    """Step time with the step's five kernels launched call by call (through the
+    Python binding, as a Python caller does) against one replay of the same step
+    captured as a HIP graph.  Times are per step over back-to-back steps between
+    two HIP events (median of 5 repetitions), so launch overhead that the GPU
+    cannot hide behind earlier work shows up in the first column.  fa_fwd,
+    fa_bwd_preprocess and fa_bwd with a caller-held workspace allocate nothing,
+    so the step is capturable as is; every replay matches the eager step bit for
+    bit (tests/test_gpu_graph.py)."""
+    from exact_attention_causal_amd.inputs import Workload, make_inputs
+    fa.load_library()
+    shapes = [WORKLOADS[n] for n in ("f32_b1h2_s128_d64", "bf16_b4h12_s512_d64", "bf16_b4h16_s2048_d64_peaky")]
+    shapes += [Workload(f"bf16_b1h1_s{S}_d128", "bf16", 1, 1, S, 128, seed=7) for S in (256, 1024, 4096)]
+    print("| workload | eager step ms | graph replay ms | speed-up | graph fwd+bwd TFLOP/s |")
+    print("|---|---|---|---|---|")
+    rows = []
+    for w in shapes:
+        B, H, S, D = w.shape
+        code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+        q, k, v, do = (x.to(dev) for x in make_inputs(B, H, S, D, w.dtype, seed=w.seed, qk_mult=w.qk_mult))
+        o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+        lse = torch.empty((B, H, S), device=dev, dtype=torch.float32)
+        delta = torch.empty_like(lse)
+        ws_bytes = fa.fa_bwd_workspace_size(B, H, S, D, code)
+        ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+
+        def step():
+            rc = fa.fa_fwd(q, k, v, o, lse, B, H, S, D, w.scale, 1, code)
+            rc = rc or fa.fa_bwd_preprocess(o, do, delta, B, H, S, D, code)
+            rc = rc or fa.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, ws, ws_bytes, B, H, S, D,
+                                 w.scale, 1, code)
+            if rc != 0:
+                raise RuntimeError(fa.fa_strerror(rc))
+
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+
+        def per_step(f, n=50):
+            ts = []
+            for _ in range(5):
+                f()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(n):
+                    f()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) / n)
+            return statistics.median(ts)
+
+        t_e, t_g = per_step(step), per_step(g.replay)
+        tf = 14 * D * w.causal_pairs() / (t_g * 1e-3) / 1e12
+        rows.append({"workload": w.name, "eager_ms": round(t_e, 5), "graph_ms": round(t_g, 5)})
+        print(f"| {w.name} | {t_e:.4f} | {t_g:.4f} | {t_e / t_g:.2f}x | {tf:.1f} |", flush=True)
+        del g
+    print(json.dumps({"graph_steps": rows}), flush=True)
+    return rows
+
+
 def vs_materialised(dev):
     """One forward+backward of this library against attention with the S x S matrix materialised.
 
@@ -464,6 +532,9 @@ def main():
         return
     if args.vs_materialised:
         vs_materialised(dev)
+        return
+    if args.graph:
+        graph_steps(dev)
         return
     if args.hold > 0:
         hold(dev, WORKLOADS[args.workload], args.hold, args.hold_entry)
