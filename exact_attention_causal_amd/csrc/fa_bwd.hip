@@ -1217,11 +1217,21 @@ BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_byt
     BwdSplit r{1, S};
     if (dtype != 1 || !head_dim_supported(D) || S <= 256) return r;
     const long long cu = ncu > 0 ? ncu : 1;
-    // one wave of dK/dV workgroups (256 keys each) per CU or less: the
-    // longest causal tile walks the whole sequence alone
+    // dK/dV workgroups of the unsplit pass (256 keys each); the longest causal
+    // one walks the whole sequence.  Splitting shortens that walk n-fold but
+    // writes and sums n sets of fp32 partials.  Measured over B*H = 1..128,
+    // S = 512..16384, D = 64/80/128 (every chunk count, interleaved): about one
+    // workgroup per CU in flight is best; at S <= 512 the walk is too short to
+    // pay for the partials unless only a few tiles exist; with one to two
+    // tiles per CU, two chunks still pay from S = 4096 on.
     const long long tiles = (long long)BH * ((S + 255) / 256);
-    if (tiles >= 2 * cu) return r;
-    long long n = (2 * cu + tiles - 1) / tiles;
+    long long n = 1;
+    if (S <= 512)
+        n = tiles * 16 <= cu ? 4 : 1;
+    else if (tiles < cu)
+        n = (cu + tiles - 1) / tiles;
+    else if (tiles < 2 * cu && S >= 4096)
+        n = 2;
     // at most 8 chunks (16 were no faster overall and hold twice the
     // partials), and no more partial results than the budget
     const long long per = 3LL * BH * S * D * 4;

@@ -246,12 +246,19 @@ def test_plan_thresholds_follow_the_cu_count(lib):
     # fp32 never takes the bf16-only tiles; wide fp32 heads use 32-key tiles
     p = _plan(1, 1, 4096, 128, f32, 256)
     assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile, p.bwd_chunks) == (256, 1, 32, 1)
-    # split backward: below 2 dK/dV tiles of 256 keys per CU, n = ceil(2 CU / tiles) <= 8 chunks
-    p = _plan(1, 1, 8192, 128, bf, 256)          # 32 tiles: 16 wanted, 8 allowed
+    # split backward: below one dK/dV tile of 256 keys per CU, n = ceil(CU / tiles) <= 8 chunks;
+    # one to two tiles per CU: 2 chunks from S = 4096 on; S <= 512: 4 chunks below CU/16 tiles
+    p = _plan(1, 1, 8192, 128, bf, 256)          # 32 tiles: 8 wanted
     assert (p.bwd_chunks, p.bwd_chunk_rows) == (8, 1024)
-    p = _plan(1, 1, 8192, 128, bf, 32)           # 32 tiles: 2 wanted
+    p = _plan(1, 16, 1024, 128, bf, 256)         # 64 tiles: 4
+    assert (p.bwd_chunks, p.bwd_chunk_rows) == (4, 256)
+    p = _plan(1, 1, 8192, 128, bf, 32)           # 32 tiles on 32 CUs, S >= 4096: 2
     assert (p.bwd_chunks, p.bwd_chunk_rows) == (2, 4096)
+    assert _plan(4, 16, 1024, 64, bf, 256).bwd_chunks == 1  # 256 tiles on 256 CUs, S < 4096
     assert _plan(1, 1, 8192, 128, bf, 16).bwd_chunks == 1   # already 2 tiles per CU
+    p = _plan(1, 1, 512, 64, bf, 256)            # S <= 512, 2 tiles: 4 chunks of 128 rows
+    assert (p.bwd_chunks, p.bwd_chunk_rows) == (4, 128)
+    assert _plan(4, 12, 512, 64, bf, 256).bwd_chunks == 1   # S <= 512, 96 tiles: the partials cost more
     p = _plan(1, 1, 65536, 128, bf, 256)         # 256 tiles: 2 wanted, 2 fit in 256 MiB
     assert (p.bwd_chunks, p.bwd_chunk_rows) == (2, 32768)
     assert _plan(1, 1, 65536, 128, bf, 128).bwd_chunks == 1

@@ -63,7 +63,7 @@ def run(B, H, S, D, dtype, seed, with_oracle):
 
 
 def test_noalloc_matches_fa_bwd_on_consecutive_calls():
-    # split backward (8 chunks fit the scratch), then a smaller problem, unsplit
+    # split backward (8 chunks fit the scratch), then a smaller problem (3 chunks)
     run(1, 2, 1500, 128, "bf16", seed=701, with_oracle=True)
     run(1, 1, 300, 64, "bf16", seed=702, with_oracle=True)
     # fp32 (never split), then smaller again
