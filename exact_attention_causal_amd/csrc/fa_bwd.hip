@@ -1092,15 +1092,21 @@ __global__ __launch_bounds__(C::NT) void dq_kernel(const T *__restrict__ q, cons
 
 // ---------------------------------------------- sum of partial results ---
 
-// out = sum of n fp32 partial results `stride` elements apart, in a fixed
+// out_g = sum of n fp32 partial results `stride` elements apart, in a fixed
 // order (so the split backward stays bit-reproducible), rounded to T; four
-// elements per thread (count4 = elements / 4).
+// elements per thread (count4 = elements / 4).  One launch for the three
+// gradients: blockIdx.y = g selects out_g, whose partials start g*n*stride
+// elements into `parts`.
 template <typename T>
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float *__restrict__ parts, int n,
-                                                        long long stride, T *__restrict__ out,
+                                                        long long stride, T *__restrict__ out0,
+                                                        T *__restrict__ out1, T *__restrict__ out2,
                                                         long long count4) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= count4) return;
+    const int g = blockIdx.y;
+    T *const out = g == 0 ? out0 : g == 1 ? out1 : out2;
+    parts += (size_t)g * n * stride;
     f32x4 acc = *reinterpret_cast<const f32x4 *>(parts + 4 * i);
     for (int p = 1; p < n; ++p) acc += *reinterpret_cast<const f32x4 *>(parts + p * stride + 4 * i);
     store4<T>(out + 4 * i, acc, 1.f);
@@ -1262,14 +1268,10 @@ int launch_bwd(int dtype, const void *q, const void *k, const void *v, const voi
         const long long count4 = (long long)(n_el / 4);
         const long long grid = (count4 + 255) / 256;
         if (grid > 0x7fffffffLL) return -1;
-        float *const src[3] = {pq, pk, pv};
-        void *const dst[3] = {dq, dk, dv};
-        for (int t = 0; t < 3; ++t) {
-            hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3((unsigned)grid), dim3(256), 0, stream, src[t], sp.n,
-                               (long long)n_el, (bf16 *)dst[t], count4);
-            if (hipGetLastError() != hipSuccess) return -5;
-        }
-        return 0;
+        // (the partials of dQ, dK, dV follow each other: pk = pq + n*n_el, pv = pk + n*n_el)
+        hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3((unsigned)grid, 3), dim3(256), 0, stream, pq, sp.n,
+                           (long long)n_el, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, count4);
+        return hipGetLastError() == hipSuccess ? 0 : -5;
     }
     const long long rows = (long long)BH * S;
     const long long grid = (rows + 255) / 256;
