@@ -497,24 +497,31 @@ FwdPlan fwd_plan(int dtype, int BH, int S, int D, int ncu) {
     // Few 256-query tiles per CU: two key groups per workgroup on 128-query
     // tiles (the longest tile walks half the keys per group). Measured
     // 1.4-1.9x faster at one tile per CU or fewer (one head, S = 1024 to
-    // 65536; four heads at S = 16384). Past that, D = 64 and 80 gain 9-14 %
-    // up to two tiles per CU and are level at 2.5; D = 96 and 128 are level
-    // at 1.5 and 10 % slower at 1.75 and 2.
+    // 65536; four heads at S = 16384).  Past one tile per CU the walk must be
+    // long enough to pay for the merge and the shorter tiles (every tile
+    // count at S = 512 .. 32768, D = 64, 80, 128): D = 64 and 80 gain 3-10 %
+    // at two tiles per CU from S = 4096 on but lose 14-18 % at S = 2048;
+    // D = 96 and 128 gain up to 1.5 tiles per CU from S = 2048 on, lose 4 %
+    // at one tile per CU at S = 1024, and are 10 % slower at 1.75 and 2.
     if (bf && D >= 64) {
         const long long tiles1 = (long long)((S + 255) / 256) * BH;
-        if (D <= 80 ? tiles1 <= 2 * cu : 2 * tiles1 <= 3 * cu) return FwdPlan{128, 2, D > 80 ? 32 : 64, 0};
+        const bool two = D <= 80 ? tiles1 <= cu || (tiles1 <= 2 * cu && S >= 4096)
+                                 : 2 * tiles1 <= cu || (2 * tiles1 <= 3 * cu && S >= 2048);
+        if (two) return FwdPlan{128, 2, D > 80 ? 32 : 64, 0};
     }
     // bf16 D=128: 64 queries per wave over 32-key tiles halves the K/V reads
-    // per FLOP, but makes the query tiles twice as long; keep it for problems
-    // with at least four such tiles per CU (short causal problems lose more
-    // to the uneven tile lengths than they gain).  Measured slower at D=80.
+    // per FLOP, but makes the query tiles twice as long: the masked half of
+    // the diagonal tile and the uneven tile lengths cost more at short
+    // sequences.  Measured against the 256-query tile: 19.6 % slower at
+    // S = 8192 with 4 tiles of 512 per CU, 2.5-6 % faster from S = 16384 on
+    // with 2 tiles per CU, 50 % slower with one.  Measured slower at D=80.
     // Its workgroups go to the XCDs head by head in bands of 64 tiles
     // (tile_order): at S = 65536, H = 16 that halves the kernel's HBM
     // traffic (FETCH_SIZE + WRITE_SIZE 9.51 -> 4.67 GB) and runs 0.5-1 %
     // faster; the same order made the D = 80 tile 4-9 % slower.
     if (bf && D == 128) {
         const long long tiles2 = (long long)((S + 511) / 512) * BH;
-        if (tiles2 >= 4 * cu) return FwdPlan{512, 1, 32, BH % kNumXcd == 0 ? 64 : 0};
+        if (S >= 16384 && tiles2 >= 2 * cu) return FwdPlan{512, 1, 32, BH % kNumXcd == 0 ? 64 : 0};
     }
     return FwdPlan{256, 1, (!bf && D > 80) ? 32 : 64, 0};
 }

@@ -226,18 +226,24 @@ def test_plan_thresholds_follow_the_cu_count(lib):
     """Tile selection is a function of the device's compute units: every threshold moves with them."""
     bf, f32 = fa.FA_BF16, fa.FA_F32
     # S=65536, D=128, 16 heads: 2048 tiles of 512 queries = 8 per CU on 256 CUs (64 queries per
-    # wave); below 4 per CU (1024 CUs) the 256-query tile; at 1.5 tiles of 256 per CU or fewer
-    # (3072 CUs and up) two key groups on 128-query tiles
+    # wave, S >= 16384); below 2 per CU (1024 CUs) the 256-query tile; at 1.5 tiles of 256 per CU
+    # or fewer (2731 CUs and up) two key groups on 128-query tiles
     p = _plan(1, 16, 65536, 128, bf, 256)
     assert (p.fwd_block_queries, p.fwd_key_tile, p.fwd_band) == (512, 32, 64)   # 16 heads: banded order
     assert _plan(1, 12, 65536, 128, bf, 256).fwd_band == 0    # 12 heads do not split over 8 XCDs
     assert _plan(1, 32, 16000, 80, bf, 256).fwd_band == 0     # D = 80: consecutive heads
-    assert _plan(1, 16, 65536, 128, bf, 512).fwd_block_queries == 512    # exactly 4 per CU
-    assert _plan(1, 16, 65536, 128, bf, 513).fwd_block_queries == 256
+    assert _plan(1, 16, 65536, 128, bf, 1024).fwd_block_queries == 512   # exactly 2 per CU
+    assert _plan(1, 16, 65536, 128, bf, 1025).fwd_block_queries == 256
+    assert _plan(1, 64, 8192, 128, bf, 256).fwd_block_queries == 256     # 4 per CU, but S < 16384
+    assert _plan(1, 64, 1024, 128, bf, 256).fwd_key_groups == 1          # one tile per CU, S < 2048
+    assert _plan(1, 32, 2048, 128, bf, 256).fwd_key_groups == 2          # one tile per CU, S >= 2048
     assert _plan(1, 16, 65536, 128, bf, 2730).fwd_key_groups == 1        # 4096 > 1.5 * 2730
     p = _plan(1, 16, 65536, 128, bf, 2731)
     assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile) == (128, 2, 32)
-    # D <= 80: two key groups up to 2 tiles of 256 per CU (32 heads of 16000: 2016 tiles)
+    # D <= 80: two key groups up to one tile of 256 per CU, and up to 2 from S = 4096 on
+    assert _plan(1, 32, 2048, 64, bf, 256).fwd_key_groups == 2          # 256 tiles
+    assert _plan(1, 64, 2048, 64, bf, 256).fwd_key_groups == 1          # 512 tiles, S < 4096
+    # (32 heads of 16000: 2016 tiles)
     assert _plan(1, 32, 16000, 80, bf, 1007).fwd_key_groups == 1
     p = _plan(1, 32, 16000, 80, bf, 1008)
     assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile) == (128, 2, 64)

@@ -219,10 +219,10 @@ def test_head_dims(D, dtype):
 
 @pytest.mark.parametrize("D", [16, 32, 64, 80, 96, 128])
 def test_head_dims_many_query_tiles(D):
-    # 512 heads x 520 rows give 1024 query tiles of 512 rows (two per head, the
-    # second ragged): enough that the bf16 D=128 forward runs 64 queries per
-    # wave, and a many-head launch for the other head dims.  Heads are
-    # independent, so the oracle checks a spread of them.
+    # 512 heads x 520 rows: a many-head launch (two key groups in the bf16
+    # forward at D >= 64, more than one dK/dV tile per CU, so no split).  Heads
+    # are independent, so the oracle checks a spread of them.  (The 512-query
+    # D = 128 forward tile needs S >= 16384: see the tests of its orders below.)
     q, k, v, do = make_inputs(1, 512, 520, D, "bf16", seed=400 + D)
     print(f"[parity] many query tiles D={D} shape={tuple(q.shape)}", flush=True)
     g = run_gpu(q, k, v, do)
@@ -699,12 +699,13 @@ def test_forward_on_a_side_stream():
 
 # ------------------------------------------- workgroup order of the forward ---
 
-def _banded_forward(B, H, S, heads, rows=None, causal=True):
-    """Forward through a launch that takes the banded XCD order (the 512-query D=128 tile,
-    B*H a multiple of 8); outputs start as NaN so a (head, tile) the order skipped shows."""
+def _banded_forward(B, H, S, heads, rows=None, causal=True, banded=True):
+    """Forward through a launch that takes the 512-query D=128 tile, in the banded XCD order
+    (B*H a multiple of 8) or the consecutive one; outputs start as NaN so a (head, tile) the
+    order skipped shows."""
     D = 128
     rc, plan = fa.fa_get_plan(B, H, S, D, fa.FA_BF16, 0)
-    assert rc == 0 and plan.fwd_block_queries == 512 and plan.fwd_band > 0, plan.as_dict()
+    assert rc == 0 and plan.fwd_block_queries == 512 and (plan.fwd_band > 0) == banded, plan.as_dict()
     print(f"[parity] banded forward B={B} H={H} S={S} band={plan.fwd_band} causal={causal}", flush=True)
     q, k, v, do = make_inputs(B, H, S, D, "bf16", seed=900 + H)
     dev = torch.device("cuda:0")
@@ -730,8 +731,21 @@ def _banded_forward(B, H, S, heads, rows=None, causal=True):
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_banded_order_partial_bands(causal):
-    # 1024 heads of 3 query tiles: every XCD's heads fall in one partial band
-    _banded_forward(2, 512, 1100, heads=[0, 1, 7, 8, 9, 513, 1016, 1023], causal=causal)
+    # 32 heads of 33 query tiles (the last one ragged): every XCD's heads fall in partial bands of
+    # 64; every (head, tile) is checked finite, sampled rows (all tile edges) against the oracle
+    S = 16384 + 100
+    edges = [r for t in range(0, S, 512) for r in (t, t + 1, t + 511) if r < S]
+    rows = sorted(set(edges + [S - 2, S - 1] + list(np.random.default_rng(33).integers(0, S, 24))))
+    _banded_forward(2, 16, S, heads=[0, 1, 7, 8, 9, 23, 31], rows=rows, causal=causal)
+
+
+def test_512_query_tile_consecutive_order():
+    # 33 heads (not a multiple of the 8 XCDs): the 512-query tile in the consecutive order,
+    # 33 tiles per head with a ragged last one of 37 rows
+    S = 16384 + 37
+    edges = [r for t in range(0, S, 512) for r in (t, t + 511) if r < S]
+    rows = sorted(set(edges + [S - 2, S - 1] + list(np.random.default_rng(34).integers(0, S, 16))))
+    _banded_forward(1, 33, S, heads=[0, 16, 32], rows=rows, banded=False)
 
 
 @pytest.mark.slow
