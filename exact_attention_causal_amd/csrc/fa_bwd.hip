@@ -200,21 +200,27 @@ __global__ __launch_bounds__(C::NT) void dkdv_kernel(const T *__restrict__ q, co
     const int role = wave / C::NPAIR;   // 0: P / dV wave, 1: dS / dK wave
     const int pair = wave % C::NPAIR;
     const int h = lane >> 5, l32 = lane & 31;
-    const int BH = a.BH, S = a.Sq, causal = a.causal;
-    const int Sk = GEN ? a.Sk : S;    // keys of the head (queries: S)
-    const int off = GEN ? a.off : 0;  // query i sits off positions after key 0
+    const int BH = a.BH, Sh = a.Sq, causal = a.causal;
+    // this launch's queries: chunk blockIdx.y of the head's query rows
+    // (key-set calls; uniform values kept in scalar registers, see the forward kernel)
+    const int qbeg = GEN ? blockIdx.y * a.qchunk : 0;
+    const int S = GEN ? __builtin_amdgcn_readfirstlane(min(a.qchunk, Sh - qbeg)) : Sh;
+    const int Sk = GEN ? a.Sk : Sh;   // keys of the head
+    // query i of the chunk sits off positions after key 0
+    const int off = GEN ? __builtin_amdgcn_readfirstlane(a.off + qbeg) : 0;
     const float c = a.c;
     const int bid = blockIdx.x;
     const int kt = bid / BH;  // ascending: the tiles with the most query tiles go first
     const int bh = bid % BH;
-    q += (size_t)bh * S * D;
-    dout += (size_t)bh * S * D;
+    q += ((size_t)bh * Sh + qbeg) * D;
+    dout += ((size_t)bh * Sh + qbeg) * D;
     k += (size_t)bh * Sk * D;
     v += (size_t)bh * Sk * D;
-    dk += (size_t)bh * Sk * D;
-    dv += (size_t)bh * Sk * D;
-    lse += (size_t)bh * S;
-    delta += (size_t)bh * S;
+    const size_t part = GEN ? (size_t)blockIdx.y * BH * Sk * D : 0;
+    dk += part + (size_t)bh * Sk * D;
+    dv += part + (size_t)bh * Sk * D;
+    lse += (size_t)bh * Sh + qbeg;
+    delta += (size_t)bh * Sh + qbeg;
     const int k0 = kt * C::BKV;
     const int kw0 = k0 + pair * 32;
     const int key = kw0 + l32;  // this lane's key column
@@ -1159,12 +1165,12 @@ static int bwd_for(const void *q, const void *k, const void *v, const void *dout
     a.nqt = (a.Sq + QC::BQ - 1) / QC::BQ;
     const long long g2 = (long long)a.nqt * a.BH;
     if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL || ny < 1 || ny > 65535) return -1;
-    if (ny > 1 && !(GEN && kv_single<T, D>())) return -1;  // (the pair kernel takes no chunks)
+    if (ny > 1 && !GEN) return -1;  // (chunks are key-set calls)
     if constexpr (kv_single<T, D>())
         hipLaunchKernelGGL((dkdv1_kernel<T, K1, OutT, GEN>), dim3((unsigned)g1, ny), dim3(K1::NT), 0, stream,
                            (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dk, dv, a);
     else
-        hipLaunchKernelGGL((dkdv_kernel<T, KC, OutT, GEN>), dim3((unsigned)g1), dim3(KC::NT), 0, stream,
+        hipLaunchKernelGGL((dkdv_kernel<T, KC, OutT, GEN>), dim3((unsigned)g1, ny), dim3(KC::NT), 0, stream,
                            (const T *)q, (const T *)k, (const T *)v, (const T *)dout, lse, delta, dk, dv, a);
     if (hipGetLastError() != hipSuccess) return -5;
     hipLaunchKernelGGL((dq_kernel<T, QC, OutT, GEN>), dim3((unsigned)g2, ny), dim3(QC::NT), 0, stream,
@@ -1221,23 +1227,35 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
 
 BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_bytes) {
     BwdSplit r{1, S};
-    if (dtype != 1 || !head_dim_supported(D) || S <= 256) return r;
+    if ((dtype != 0 && dtype != 1) || !head_dim_supported(D) || S <= 256) return r;
     const long long cu = ncu > 0 ? ncu : 1;
-    // dK/dV workgroups of the unsplit pass (256 keys each); the longest causal
-    // one walks the whole sequence.  Splitting shortens that walk n-fold but
-    // writes and sums n sets of fp32 partials.  Measured over B*H = 1..128,
-    // S = 512..16384, D = 64/80/128 (every chunk count, interleaved): about one
-    // workgroup per CU in flight is best; at S <= 512 the walk is too short to
-    // pay for the partials unless only a few tiles exist; with one to two
-    // tiles per CU, two chunks still pay from S = 4096 on.
-    const long long tiles = (long long)BH * ((S + 255) / 256);
+    // The longest causal dK/dV workgroup walks the whole sequence.  Splitting
+    // shortens that walk n-fold but writes and sums n sets of fp32 partials.
+    // The counts below were measured (every chunk count, interleaved).
     long long n = 1;
-    if (S <= 512)
-        n = tiles * 16 <= cu ? 4 : 1;
-    else if (tiles < cu)
-        n = (cu + tiles - 1) / tiles;
-    else if (tiles < 2 * cu && S >= 4096)
-        n = 2;
+    if (dtype == 1) {
+        // bf16, 256 keys per dK/dV workgroup.  Over B*H = 1..128, S = 512..16384,
+        // D = 64/80/128: about one workgroup per CU in flight is best; at
+        // S <= 512 the walk is too short to pay for the partials unless only
+        // a few tiles exist; with one to two tiles per CU, two chunks still
+        // pay from S = 4096 on.
+        const long long tiles = (long long)BH * ((S + 255) / 256);
+        if (S <= 512)
+            n = tiles * 16 <= cu ? 4 : 1;
+        else if (tiles < cu)
+            n = (cu + tiles - 1) / tiles;
+        else if (tiles < 2 * cu && S >= 4096)
+            n = 2;
+    } else {
+        // fp32, 128 keys per (pair) dK/dV workgroup; each step is long (fp32
+        // matrix cores), so splitting pays more and at more workgroups.  Over
+        // B*H = 1..32, S = 512..16384, D = 64 and 128 (2.3-6.8x faster below
+        // one workgroup per CU): 8 chunks up to a quarter workgroup per CU or
+        // while the walk is long (S >= 32 tiles), 4 up to half, 2 up to two
+        // per CU -- within 5 % of the best count at every measured point.
+        const long long t = (long long)BH * ((S + 127) / 128);
+        n = (4 * t <= cu || 32 * t <= S) ? 8 : 2 * t <= cu ? 4 : t <= 2 * cu ? 2 : 1;
+    }
     // at most 8 chunks (16 were no faster overall and hold twice the
     // partials), and no more partial results than the budget
     const long long per = 3LL * BH * S * D * 4;
@@ -1256,7 +1274,6 @@ int launch_bwd(int dtype, const void *q, const void *k, const void *v, const voi
     if (dtype != 0 && dtype != 1) return -2;
     if (!head_dim_supported(D)) return -2;
     if (sp.n > 1) {
-        if (dtype != 1) return -1;  // (bwd_split splits bf16 problems only)
         // Few key tiles for the CUs: dK/dV over sp.n query chunks and dQ over
         // sp.n key chunks run side by side as key-set products (natural-log L,
         // fp32 partials in the workspace after the lse2 region), then summed.
@@ -1264,13 +1281,19 @@ int launch_bwd(int dtype, const void *q, const void *k, const void *v, const voi
         float *parts = lse2 + bwd_lse2_bytes((long long)BH * S) / sizeof(float);
         float *pq = parts, *pk = parts + (size_t)sp.n * n_el, *pv = parts + 2 * (size_t)sp.n * n_el;
         const BwdShape a{BH, S, S, 0, causal, 0, 0, scale * kLog2e, scale, sp.chunk, sp.chunk, 0};
-        FA_D_SWITCH_INT(D, (bwd_for<bf16, DD, float, true>(q, k, v, dout, lse, delta, pq, pk, pv, a, stream, sp.n)))
         const long long count4 = (long long)(n_el / 4);
         const long long grid = (count4 + 255) / 256;
         if (grid > 0x7fffffffLL) return -1;
         // (the partials of dQ, dK, dV follow each other: pk = pq + n*n_el, pv = pk + n*n_el)
-        hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3((unsigned)grid, 3), dim3(256), 0, stream, pq, sp.n,
-                           (long long)n_el, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, count4);
+        if (dtype == 1) {
+            FA_D_SWITCH_INT(D, (bwd_for<bf16, DD, float, true>(q, k, v, dout, lse, delta, pq, pk, pv, a, stream, sp.n)))
+            hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3((unsigned)grid, 3), dim3(256), 0, stream, pq, sp.n,
+                               (long long)n_el, (bf16 *)dq, (bf16 *)dk, (bf16 *)dv, count4);
+        } else {
+            FA_D_SWITCH_INT(D, (bwd_for<float, DD, float, true>(q, k, v, dout, lse, delta, pq, pk, pv, a, stream, sp.n)))
+            hipLaunchKernelGGL(sum_parts_kernel<float>, dim3((unsigned)grid, 3), dim3(256), 0, stream, pq, sp.n,
+                               (long long)n_el, (float *)dq, (float *)dk, (float *)dv, count4);
+        }
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }
     const long long rows = (long long)BH * S;

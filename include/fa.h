@@ -92,13 +92,14 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
  * Bytes of device workspace fa_bwd needs for these sizes: B*H*S fp32 values
  * (rounded up to 256 bytes), where fa_bwd keeps lse in base 2 (L * log2 e)
  * so that recomputing P = 2^(S * scale * log2 e - L * log2 e) costs no
- * multiply per probability.  For bf16 problems with too few key tiles to
- * fill the GPU (B*H*ceil(S/256) below twice the device's compute units, and
- * S > 256), fa_bwd can instead cut each pass into n chunks (n <= 8, 64-row
- * multiples) that run side by side and sum their fp32 partial dQ, dK, dV in
- * a fixed order (still bit-reproducible): the size returned then adds
- * 3*n*B*H*S*D fp32 values (at most 256 MiB).  The compute-unit count is the
- * current device's (that of one MI355X, 256, when no device is visible).
+ * multiply per probability.  For problems with too few key tiles to fill
+ * the GPU (S > 256; the chunk count follows the number of dK/dV workgroups
+ * per compute unit and S, as fa_get_plan reports it), fa_bwd can instead cut
+ * each pass into n chunks (n <= 8, 64-row multiples) that run side by side
+ * and sum their fp32 partial dQ, dK, dV in a fixed order (still
+ * bit-reproducible): the size returned then adds 3*n*B*H*S*D fp32 values
+ * (at most 256 MiB).  The compute-unit count is the current device's (that
+ * of one MI355X, 256, when no device is visible).
  * Returns 0 for invalid sizes; fa_bwd reports those.
  */
 size_t fa_bwd_workspace_size(int B, int H, int S, int D, int dtype);

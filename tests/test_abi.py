@@ -55,7 +55,7 @@ def test_strerror(lib):
 def test_workspace_size(lib):
     # one fp32 per row (the base-2 copy of lse), rounded up to 256 bytes; 0 for invalid sizes
     assert fa.fa_bwd_workspace_size(1, 16, 65536, 128, fa.FA_BF16) == 16 * 65536 * 4
-    assert fa.fa_bwd_workspace_size(4, 12, 512, 64, fa.FA_F32) == 4 * 12 * 512 * 4
+    assert fa.fa_bwd_workspace_size(4, 12, 512, 64, fa.FA_F32) == 48 * 512 * 4 + 3 * 2 * 48 * 512 * 64 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, fa.FA_BF16) == 256
     assert fa.fa_bwd_workspace_size(1, 1, 0, 64, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 128, 72, fa.FA_BF16) == 0
@@ -64,7 +64,9 @@ def test_workspace_size(lib):
     assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_BF16) == 8192 * 4 + 3 * 8 * 8192 * 128 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 65536, 128, fa.FA_BF16) == 65536 * 4 + 3 * 2 * 65536 * 128 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 1000, 80, fa.FA_BF16) == 4096 + 3 * 8 * 1000 * 80 * 4
-    assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_F32) == 8192 * 4          # fp32: never split
+    # fp32: 128-key dK/dV workgroups, split more readily (64 tiles: 8 chunks)
+    assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_F32) == 8192 * 4 + 3 * 8 * 8192 * 128 * 4
+    assert fa.fa_bwd_workspace_size(4, 32, 8192, 128, fa.FA_F32) == 128 * 8192 * 4  # 8192 tiles
     assert fa.fa_bwd_workspace_size(2, 16, 8192, 128, fa.FA_BF16) == 32 * 8192 * 4   # enough tiles
 
 
@@ -251,7 +253,13 @@ def test_plan_thresholds_follow_the_cu_count(lib):
     assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile) == (256, 1, 64)
     # fp32 never takes the bf16-only tiles; wide fp32 heads use 32-key tiles
     p = _plan(1, 1, 4096, 128, f32, 256)
-    assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile, p.bwd_chunks) == (256, 1, 32, 1)
+    assert (p.fwd_block_queries, p.fwd_key_groups, p.fwd_key_tile, p.bwd_chunks) == (256, 1, 32, 8)
+    # fp32 split: t = B*H*ceil(S/128) dK/dV workgroups; 8 chunks up to CU/4 or S/32, 4 up to CU/2,
+    # 2 up to 2 CU
+    assert _plan(1, 16, 1024, 64, f32, 256).bwd_chunks == 4     # t = 128
+    assert _plan(1, 32, 1024, 64, f32, 256).bwd_chunks == 2     # t = 256
+    assert _plan(1, 4, 8192, 64, f32, 256).bwd_chunks == 8      # t = 256 <= S/32
+    assert _plan(1, 32, 4096, 64, f32, 256).bwd_chunks == 1     # t = 1024
     # split backward: below one dK/dV tile of 256 keys per CU, n = ceil(CU / tiles) <= 8 chunks;
     # one to two tiles per CU: 2 chunks from S = 4096 on; S <= 512: 4 chunks below CU/16 tiles
     p = _plan(1, 1, 8192, 128, bf, 256)          # 32 tiles: 8 wanted

@@ -673,8 +673,12 @@ def test_noncontiguous_inputs():
     check_full(qt, kt, vt, dot, "bf16", causal=True, label="non-contiguous")
 
 
-def test_backward_is_deterministic():
-    q, k, v, do = make_inputs(1, 4, 1000, 80, "bf16", seed=13)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_is_deterministic(dtype):
+    # (both split: 4 heads of 1000 rows have few dK/dV tiles for the CUs)
+    q, k, v, do = make_inputs(1, 4, 1000, 80, dtype, seed=13)
+    rc, plan = fa.fa_get_plan(1, 4, 1000, 80, fa.FA_BF16 if dtype == "bf16" else fa.FA_F32, 0)
+    assert rc == 0 and plan.bwd_chunks > 1, plan.as_dict()
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
     o, lse = fa.forward(qd, kd, vd)
@@ -764,6 +768,16 @@ def test_plan_uses_the_device_cu_count():
     assert rc == 0 and plan.num_cu == n, (rc, plan.as_dict(), n)
     rc2, explicit = fa.fa_get_plan(1, 16, 65536, 128, fa.FA_BF16, n)
     assert rc2 == 0 and explicit.as_dict() == plan.as_dict()
+
+
+def test_fp32_split_backward_one_head():
+    # one fp32 head: the pair dK/dV kernel over 8 query chunks and dQ over 8 key chunks (ragged
+    # last chunk), fp32 partials summed; element by element against the oracle at 1e-4
+    B, H, S, D = 1, 1, 2000, 64
+    rc, plan = fa.fa_get_plan(B, H, S, D, fa.FA_F32, 0)
+    assert rc == 0 and plan.bwd_chunks == 8, plan.as_dict()
+    q, k, v, do = make_inputs(B, H, S, D, "f32", seed=812)
+    check_full(q, k, v, do, "f32", causal=True, label="fp32 split backward")
 
 
 def test_backward_with_a_partial_split_workspace():
