@@ -282,8 +282,9 @@ def sweep(dev):
     """Latency sweep over the grid of the handout's FlashAttention-2 benchmark.
 
     One head (B=1, H=1) per point, as in that benchmark; times are medians of
-    HIP-event times over repeated calls after warm-up.  fwd = fa_fwd;
-    fwd+bwd = fa_fwd + fa_bwd_preprocess + fa_bwd.
+    HIP-event times over repeated calls after warm-up.  fwd = fa_fwd_ws (fa_fwd
+    with the workspace its size query asks for: it splits the keys of few-tile
+    problems); fwd+bwd = that + fa_bwd_preprocess + fa_bwd.
     """
     from exact_attention_causal_amd.inputs import make_inputs
     fa.load_library()
@@ -306,10 +307,13 @@ def sweep(dev):
                     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
                     ws_bytes = fa.fa_bwd_workspace_size(1, 1, S, D, code)
                     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
+                    fws_bytes = fa.fa_fwd_workspace_size(1, 1, S, D, code)
+                    fws = torch.empty(max(fws_bytes, 1), device=dev, dtype=torch.uint8)
                     scale = 1.0 / math.sqrt(D)
 
                     def fwd():
-                        rc = fa.fa_fwd(q, k, v, o, lse, 1, 1, S, D, scale, causal, code, sh)
+                        rc = fa.fa_fwd_ws(q, k, v, o, lse, fws, fws_bytes, 1, 1, S, D, scale, causal,
+                                          code, sh)
                         assert rc == 0, fa.fa_strerror(rc)
 
                     def step():
@@ -360,7 +364,7 @@ def sweep(dev):
                     peak = (torch.cuda.max_memory_allocated() - base) / 2**20
                     # (this step's buffers were allocated before `base`; report all of them)
                     peak += sum(t.numel() * t.element_size()
-                                for t in (o, lse, delta, dq, dk, dv, ws)) / 2**20
+                                for t in (o, lse, delta, dq, dk, dv, ws)) / 2**20 + fws_bytes / 2**20
                     sxs = S * S * 4 / 2**20
                     pairs = S * (S + 1) // 2 if causal else S * S
                     tf_f = 4 * D * pairs / (t_f * 1e-3) / 1e12

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "fa.h"
@@ -88,6 +89,44 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     const int ncu = fa::stream_cu_count(stream);
     if (ncu <= 0) return FA_EHIP;
     return map_launch(fa::launch_fwd(dtype, q, k, v, o, lse, B * H, S, D, scale, causal, ncu, stream));
+}
+
+size_t fa_fwd_workspace_size(int B, int H, int S, int D, int dtype) {
+    if (check_shape(B, H, S, D, dtype) != FA_OK) return 0;
+    int ncu = fa::stream_cu_count(nullptr);
+    if (ncu <= 0) ncu = kAssumedCU;
+    const int n = fa::fwd_split(dtype, B * H, S, D, 1, ncu, fa::kMaxSplitBytes);  // (causal: the most chunks)
+    return fa::fwd_part_bytes(n, (long long)B * H, S, D);
+}
+
+int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
+              size_t workspace_bytes, int B, int H, int S, int D, float scale, int causal, int dtype,
+              hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_EINVAL;
+    if (causal != 0 && causal != 1) return FA_EINVAL;
+    if (int rc = check_scale(scale)) return rc;
+    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_EALIGN;
+    if (workspace && !aligned16(workspace)) return FA_EALIGN;
+    if ((long long)((S + 255) / 256) * B * H > 0x7fffffffLL) return FA_EINVAL;
+    const int ncu = fa::stream_cu_count(stream);
+    if (ncu <= 0) return FA_EHIP;
+    const long long BH = (long long)B * H;
+    // as many key chunks as the rule asks for and the workspace holds (1: the plain forward)
+    const int n = fa::fwd_split(dtype, (int)BH, S, D, causal, ncu,
+                                workspace ? std::min(workspace_bytes, fa::kMaxSplitBytes) : 0);
+    if (n <= 1) return map_launch(fa::launch_fwd(dtype, q, k, v, o, lse, (int)BH, S, D, scale, causal, ncu, stream));
+    // chunks of whole 64-key tiles; the partials: O parts, then L parts
+    const int chunk = 64 * ((S + 64 * n - 1) / (64 * n));
+    const int parts = (S + chunk - 1) / chunk;
+    float *o_parts = static_cast<float *>(workspace);
+    float *lse_parts = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                                 fa::fwd_part_o_bytes(parts, BH, S, D));
+    int rc = fa::launch_fwd_partial(dtype, q, k, v, o_parts, lse_parts, (int)BH, S, S, D, scale, causal, 0,
+                                    parts, chunk, stream);
+    if (rc != 0) return map_launch(rc);
+    return map_launch(fa::launch_merge(dtype, o_parts, lse_parts, parts, o, lse, BH * S, D, stream));
 }
 
 int fa_bwd_preprocess(const void *o, const void *dout, float *delta, int B, int H, int S, int D,

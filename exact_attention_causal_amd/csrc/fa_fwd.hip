@@ -34,6 +34,8 @@
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
+#include <algorithm>
+
 namespace fa {
 
 // NG = 2 (problems with few query tiles): the waves form two groups that
@@ -524,6 +526,33 @@ FwdPlan fwd_plan(int dtype, int BH, int S, int D, int ncu) {
         if (S >= 16384 && tiles2 >= 2 * cu) return FwdPlan{512, 1, 32, BH % kNumXcd == 0 ? 64 : 0};
     }
     return FwdPlan{256, 1, (!bf && D > 80) ? 32 : 64, 0};
+}
+
+int fwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t max_part_bytes) {
+    if ((dtype != 0 && dtype != 1) || !head_dim_supported(D)) return 1;
+    const long long cu = ncu > 0 ? ncu : 1;
+    // 256-query tiles of the plain forward; the longest causal one walks all
+    // keys.  Key chunks shorten that walk n-fold at the price of writing and
+    // merging n fp32 partial results.  Measured against the plain forward
+    // (every chunk count 2..32; B*H = 1..32, S = 512..32768, D = 64, 128):
+    const long long tiles = (long long)BH * ((S + 255) / 256);
+    long long n = 1;
+    if (dtype == 1) {
+        // bf16 (whose forward already runs two key groups when tiles are
+        // few): only long walks over very few tiles gain, 1.1-2.3x
+        if (S >= 2048 && 4 * tiles <= cu && 64 * tiles <= S) n = 8 * tiles <= cu ? 8 : 4;
+    } else {
+        // fp32 (long steps, no two-group tile): 1.5-10x up to one tile per CU
+        if (8 * tiles <= cu)
+            n = (cu + tiles - 1) / tiles;
+        else if (2 * tiles <= cu)
+            n = S >= 4096 ? 16 : 4;
+        else if (tiles <= cu && causal)
+            n = 2;  // (the causal imbalance of one tile per CU; level or slower without it)
+    }
+    n = std::min<long long>(n, std::min<long long>(32, S / 64));  // chunks of 64 keys or more
+    while (n > 1 && fwd_part_bytes((int)n, BH, S, D) > max_part_bytes) --n;
+    return n < 2 ? 1 : (int)n;
 }
 
 // Launch tile C if it is the one the plan names.

@@ -34,6 +34,20 @@ struct FwdPlan {
 };
 FwdPlan fwd_plan(int dtype, int BH, int S, int D, int ncu);
 
+// Key chunks for a self-attention forward that has a workspace (fa_fwd_ws):
+// 1 runs the plain forward; n > 1 runs n key chunks side by side (fp32
+// partial O and L, fwd_part_bytes of them) and merges them.  At most as many
+// chunks as max_part_bytes holds.
+int fwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t max_part_bytes);
+// Bytes of the partials of n chunks: O parts, then L parts, each rounded up to 256 bytes.
+inline size_t fwd_part_o_bytes(int n, long long BH, int S, int D) {
+    return ((size_t)n * BH * S * D * sizeof(float) + 255) & ~(size_t)255;
+}
+inline size_t fwd_part_bytes(int n, long long BH, int S, int D) {
+    if (n <= 1) return 0;
+    return fwd_part_o_bytes(n, BH, S, D) + (((size_t)n * BH * S * sizeof(float) + 255) & ~(size_t)255);
+}
+
 // Each returns 0 on success, -2 (unsupported D/dtype) or -5 (launch refused).
 // Sizes are already validated; BH = B*H; ncu as stream_cu_count.
 int launch_fwd(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
@@ -51,7 +65,7 @@ int launch_merge(int dtype, const float *o_parts, const float *lse_parts, int n,
 int launch_delta(int dtype, const void *o, const void *dout, float *delta, int BH, int S, int D,
                  hipStream_t stream);
 
-// How the bf16 backward of a problem with few key tiles per CU is split: n
+// How the backward of a problem with few key tiles per CU is split: n
 // chunks of `chunk` rows per pass (n = 1: not split), with at most
 // `max_part_bytes` of fp32 partial results.
 struct BwdSplit {

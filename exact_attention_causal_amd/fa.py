@@ -1,8 +1,9 @@
 """ctypes binding of the gfx950 attention library (include/fa.h).
 
-The functions named like the C entry points (fa_fwd, fa_bwd_preprocess,
-fa_bwd_workspace_size, fa_bwd, fa_bwd_noalloc, fa_fwd_partial, fa_merge, fa_bwd_partial,
-fa_get_plan, fa_strerror) only marshal arguments: tensors
+The functions named like the C entry points (fa_fwd, fa_fwd_workspace_size,
+fa_fwd_ws, fa_bwd_preprocess, fa_bwd_workspace_size, fa_bwd, fa_bwd_noalloc,
+fa_fwd_partial, fa_merge, fa_bwd_partial, fa_get_plan, fa_strerror) only
+marshal arguments: tensors
 become device pointers, the stream becomes HIP's stream handle, and the status
 code comes back unchanged.  ``forward`` / ``backward`` / ``attention_fwd_bwd``
 are conveniences that allocate outputs with PyTorch (device memory is the
@@ -70,6 +71,10 @@ def load_library():
     lib = ctypes.CDLL(LIB_PATH)
     lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp]
     lib.fa_fwd.restype = _i
+    lib.fa_fwd_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+    lib.fa_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_ws.argtypes = [_vp] * 6 + [ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _i, _vp]
+    lib.fa_fwd_ws.restype = _i
     lib.fa_bwd_preprocess.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     lib.fa_bwd_preprocess.restype = _i
     lib.fa_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i]
@@ -113,6 +118,17 @@ def _stream(stream):
 def fa_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype, stream=None):
     return load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D,
                                  float(scale), int(causal), int(dtype), _stream(stream))
+
+
+def fa_fwd_workspace_size(B, H, S, D, dtype):
+    return int(load_library().fa_fwd_workspace_size(B, H, S, D, int(dtype)))
+
+
+def fa_fwd_ws(q, k, v, o, lse, workspace, workspace_bytes, B, H, S, D, scale, causal, dtype,
+              stream=None):
+    return load_library().fa_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                                    int(workspace_bytes), B, H, S, D, float(scale), int(causal),
+                                    int(dtype), _stream(stream))
 
 
 def fa_bwd_preprocess(o, dout, delta, B, H, S, D, dtype, stream=None):
@@ -219,11 +235,14 @@ def _workspace(workspace, device):
     return workspace.numel() * workspace.element_size()
 
 
-def forward(q, k, v, causal=True, scale=None, out=None, lse=None, stream=None):
+def forward(q, k, v, causal=True, scale=None, out=None, lse=None, workspace=None, stream=None):
     """O, L for [B, H, S, D] q, k, v (bf16 or fp32, same shape) on the GPU.
 
     A caller's ``out`` ([B, H, S, D], q's dtype) and ``lse`` ([B, H, S] fp32) must be
-    contiguous tensors on q's device; they are overwritten.
+    contiguous tensors on q's device; they are overwritten.  ``workspace``: None
+    allocates what fa_fwd_workspace_size asks for and calls fa_fwd_ws (which splits
+    the keys of few-tile problems); False calls fa_fwd; a contiguous tensor on q's
+    device is passed to fa_fwd_ws as it is.
     """
     B, H, S, D = _shape(q)
     code = dtype_code(q.dtype)
@@ -233,6 +252,9 @@ def forward(q, k, v, causal=True, scale=None, out=None, lse=None, stream=None):
         _like("out", out, q.shape, q.dtype, q.device, contiguous=True)
     if lse is not None:
         _like("lse", lse, (B, H, S), torch.float32, q.device, contiguous=True)
+    ws_bytes = 0
+    if workspace is not None and workspace is not False:
+        ws_bytes = _workspace(workspace, q.device)
     _on_gpu(q)
     q, k, v = (x.contiguous() for x in (q, k, v))
     if scale is None:
@@ -241,7 +263,15 @@ def forward(q, k, v, causal=True, scale=None, out=None, lse=None, stream=None):
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, S), device=q.device, dtype=torch.float32)
-    _check(fa_fwd(q, k, v, out, lse, B, H, S, D, scale, causal, code, stream), "fa_fwd")
+    if workspace is False:
+        _check(fa_fwd(q, k, v, out, lse, B, H, S, D, scale, causal, code, stream), "fa_fwd")
+        return out, lse
+    if workspace is None:
+        ws_bytes = fa_fwd_workspace_size(B, H, S, D, code)
+        if ws_bytes > 0:
+            workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    _check(fa_fwd_ws(q, k, v, out, lse, workspace, ws_bytes, B, H, S, D, scale, causal, code, stream),
+           "fa_fwd_ws")
     return out, lse
 
 

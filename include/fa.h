@@ -80,6 +80,37 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            hipStream_t stream);
 
 /*
+ * Bytes of device workspace fa_fwd_ws can use for these sizes: 0 when it runs
+ * as fa_fwd; otherwise n*B*H*S*(D+1) fp32 partial values (two regions, each
+ * rounded up to 256 bytes; at most 256 MiB), for problems with few query
+ * tiles per compute unit, whose longest causal tile would walk every key
+ * alone (the size is that of causal = 1, which splits most; a non-causal call
+ * may take fewer chunks).  The compute-unit count is the current device's (256, that of one
+ * MI355X, when no device is visible).  Returns 0 for invalid sizes too.
+ */
+size_t fa_fwd_workspace_size(int B, int H, int S, int D, int dtype);
+
+/*
+ * fa_fwd with a caller workspace (same arguments, results and errors, plus
+ * the workspace).  When the keys of a problem are worth splitting, it cuts
+ * them into n chunks of whole 64-key tiles that run side by side as
+ * fa_fwd_partial does, then merges the chunks' (O, L) exactly as fa_merge
+ * does (the page "[Attention]FlashAttention/Ring-Attention/混合序列并行的统一原理",
+ * sections "online softmax" and "online attention"; handout section 4.2.2 for
+ * the forward itself).  The result
+ * equals fa_fwd's up to the order of fp32 sums; it is deterministic.
+ *   workspace : device memory of fa_fwd_workspace_size() bytes, 16-byte
+ *               aligned, or NULL (then, or with fewer bytes than one split
+ *               needs, it runs as fa_fwd; with fewer than the full size it
+ *               takes as many chunks as fit).  Contents on entry do not
+ *               matter; calls sharing a workspace must be ordered on one
+ *               stream.
+ */
+int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
+              size_t workspace_bytes, int B, int H, int S, int D, float scale, int causal, int dtype,
+              hipStream_t stream);
+
+/*
  * Backward preprocessing (handout Algorithm 2, its first step, and the text
  * before Eq. 13): delta_i = sum_d o_id * dout_id, accumulated in fp32 from
  * the stored forward output o.

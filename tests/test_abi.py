@@ -35,8 +35,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_noalloc", "fa_bwd_partial", "fa_bwd_preprocess",
-                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_partial", "fa_get_plan",
-                                     "fa_merge", "fa_strerror"]
+                                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_partial",
+                                     "fa_fwd_workspace_size", "fa_fwd_ws", "fa_get_plan", "fa_merge",
+                                     "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -105,6 +106,41 @@ def _bwd(**kw):
 ])
 def test_fwd_rejects(lib, bad, code):
     assert _fwd(**bad) == code
+    # fa_fwd_ws checks the same arguments first (with and without a workspace)
+    assert _fwd_ws(**bad) == code
+    assert _fwd_ws(workspace=None, workspace_bytes=0, **bad) == code
+
+
+def _fwd_ws(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, workspace=P, workspace_bytes=1 << 20, B=1, H=2, S=128, D=64,
+             scale=0.125, causal=1, dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_ws(**a)
+
+
+def test_fwd_ws_rejects_a_misaligned_workspace(lib):
+    assert _fwd_ws(workspace=MIS) == fa.FA_EALIGN
+
+
+def test_fwd_workspace_size(lib):
+    # 0 where fa_fwd_ws runs as fa_fwd; else n chunks of fp32 partial O and L (two regions,
+    # each rounded up to 256 bytes)
+    assert fa.fa_fwd_workspace_size(1, 16, 65536, 128, fa.FA_BF16) == 0      # many tiles
+    assert fa.fa_fwd_workspace_size(1, 1, 1024, 128, fa.FA_BF16) == 0        # bf16: S < 2048
+    # bf16, one head of 4096 (16 tiles of 256): 8 chunks
+    assert fa.fa_fwd_workspace_size(1, 1, 4096, 128, fa.FA_BF16) == 8 * 4096 * 128 * 4 + 8 * 4096 * 4
+    # bf16, 48 tiles: 4 chunks
+    assert fa.fa_fwd_workspace_size(1, 3, 4096, 64, fa.FA_BF16) == 4 * 3 * 4096 * 64 * 4 + 4 * 3 * 4096 * 4
+    # fp32, 32 tiles: ceil(256/32) = 8 chunks; 64 tiles at S >= 4096: 16; 256 tiles: 2
+    assert fa.fa_fwd_workspace_size(1, 1, 8192, 128, fa.FA_F32) == 8 * 8192 * 128 * 4 + 8 * 8192 * 4
+    assert fa.fa_fwd_workspace_size(1, 4, 4096, 64, fa.FA_F32) == 16 * 4 * 4096 * 64 * 4 + 16 * 4 * 4096 * 4
+    assert fa.fa_fwd_workspace_size(1, 16, 4096, 64, fa.FA_F32) == 2 * 16 * 4096 * 64 * 4 + 2 * 16 * 4096 * 4
+    # fp32, one head of 512: ceil(256/2) = 128 wanted, at most S/64 = 8 chunks of 64 keys
+    assert fa.fa_fwd_workspace_size(1, 1, 512, 64, fa.FA_F32) == 8 * 512 * 64 * 4 + 8 * 512 * 4
+    # at most 256 MiB of partials: one head of 32768, D = 128 wants 16 chunks (270 MB); 15 fit
+    assert fa.fa_fwd_workspace_size(1, 1, 32768, 128, fa.FA_F32) == 15 * 32768 * 128 * 4 + 15 * 32768 * 4
+    assert fa.fa_fwd_workspace_size(1, 1, 0, 64, fa.FA_BF16) == 0
+    assert fa.fa_fwd_workspace_size(1, 1, 128, 72, fa.FA_BF16) == 0
 
 
 @pytest.mark.parametrize("bad,code", [

@@ -39,6 +39,7 @@ def test_forward_mismatches():
     raises("lse has dtype", fa.forward, q, k, v, lse=t(B, H, S))
     raises(r"expected \[B, H, S, D\]", fa.forward, t(H, S, D), k, v)
     raises("unsupported dtype", fa.forward, *(x.half() for x in (q, k, v)))
+    raises("workspace must be", fa.forward, q, k, v, workspace=b"\0" * 64)
     # consistent tensors reach the device check (there is no CPU path)
     raises("must be on a GPU", fa.forward, q, k, v)
 

@@ -365,6 +365,86 @@ def test_split_kv_forward_end_to_end(n_split, S, D):
     assert rel(o.double().cpu().numpy(), o1.double().cpu().numpy()) <= 1e-2
 
 
+# ------------------------------------------------ forward with a workspace ---
+
+def _fwd_ws(q, k, v, causal, ws_bytes=None):
+    """fa_fwd_ws through the C ABI with a workspace of ws_bytes (None: the size query's)."""
+    B, H, S, D = q.shape
+    code = fa.FA_BF16 if q.dtype == torch.bfloat16 else fa.FA_F32
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, H, S), float("nan"), device=dev)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_fwd_workspace_size(B, H, S, D, code)
+    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    rc = fa.fa_fwd_ws(qd, kd, vd, o, lse, ws if ws_bytes else None, ws_bytes, B, H, S, D,
+                      1.0 / np.sqrt(D), causal, code)
+    assert rc == fa.FA_OK, fa.fa_strerror(rc)
+    o1 = torch.full_like(qd, float("nan"))
+    l1 = torch.full((B, H, S), float("nan"), device=dev)
+    rc = fa.fa_fwd(qd, kd, vd, o1, l1, B, H, S, D, 1.0 / np.sqrt(D), causal, code)
+    assert rc == fa.FA_OK
+    torch.cuda.synchronize()
+    return o, lse, o1, l1
+
+
+@pytest.mark.parametrize("B,H,S,D,dtype,causal", [
+    (1, 1, 4096, 128, "bf16", 1),   # 16 tiles: 8 key chunks
+    (1, 3, 2100, 64, "bf16", 1),    # 27 tiles, ragged: 7 chunks of 320 keys
+    (2, 1, 1000, 80, "f32", 1),     # 8 tiles: 8 chunks of 128 keys (16-row tails)
+    (1, 2, 777, 32, "f32", 0),      # non-causal, ragged: 7 chunks
+    (1, 4, 4096, 64, "f32", 1),     # 64 tiles at S >= 4096: 16 chunks
+])
+def test_fwd_ws_split_matches_oracle(B, H, S, D, dtype, causal):
+    code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
+    nb = fa.fa_fwd_workspace_size(B, H, S, D, code)
+    assert nb > 0
+    print(f"[parity] fa_fwd_ws B={B} H={H} S={S} D={D} {dtype} causal={causal} ws={nb}", flush=True)
+    q, k, v, _ = make_inputs(B, H, S, D, dtype, seed=1300 + S)
+    o, lse, o1, l1 = _fwd_ws(q, k, v, causal)
+    r_o, r_l = oracle.forward(*(x.double().numpy() for x in (q, k, v)), causal=bool(causal))
+    go, gl = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    assert rel(go, r_o) <= TOL[dtype]["o"], rel(go, r_o)
+    assert absdiff(gl, r_l) <= TOL[dtype]["lse"], absdiff(gl, r_l)
+    # the same attention as fa_fwd, up to the order of fp32 sums (and bf16 rounding of O)
+    assert rel(go, o1.double().cpu().numpy()) <= (1e-5 if dtype == "f32" else 1e-2)
+
+
+def test_fwd_ws_runs_as_fa_fwd_without_a_split():
+    # no split wanted (many tiles), no workspace, or one too small for two chunks:
+    # bit-identical to fa_fwd
+    q, k, v, _ = make_inputs(1, 16, 1024, 64, "bf16", seed=1401)
+    assert fa.fa_fwd_workspace_size(1, 16, 1024, 64, fa.FA_BF16) == 0
+    o, lse, o1, l1 = _fwd_ws(q, k, v, 1)
+    assert torch.equal(o, o1) and torch.equal(lse, l1)
+    q, k, v, _ = make_inputs(1, 1, 4096, 128, "bf16", seed=1402)
+    for nb in (0, 4096 * 129 * 4):   # none; one chunk's worth (two do not fit)
+        o, lse, o1, l1 = _fwd_ws(q, k, v, 1, ws_bytes=nb)
+        assert torch.equal(o, o1) and torch.equal(lse, l1), nb
+
+
+def test_fwd_ws_with_a_partial_workspace():
+    # a workspace for 3 of the 8 chunks the size query asks for takes 3 chunks
+    B, H, S, D = 1, 1, 4096, 128
+    q, k, v, _ = make_inputs(B, H, S, D, "bf16", seed=1403)
+    nb = 3 * S * D * 4 + 3 * S * 4 + 512
+    o, lse, o1, _ = _fwd_ws(q, k, v, 1, ws_bytes=nb)
+    r_o, r_l = oracle.forward(*(x.double().numpy() for x in (q, k, v)), causal=True)
+    assert rel(o.double().cpu().numpy(), r_o) <= TOL["bf16"]["o"]
+    assert absdiff(lse.double().cpu().numpy(), r_l) <= TOL["bf16"]["lse"]
+    assert not torch.equal(o, o1)   # (it did split)
+
+
+def test_fwd_ws_is_deterministic():
+    q, k, v, _ = make_inputs(2, 1, 3000, 64, "f32", seed=1404)
+    first = _fwd_ws(q, k, v, 1)[:2]
+    for _ in range(2):
+        again = _fwd_ws(q, k, v, 1)[:2]
+        assert all(torch.equal(a, b) for a, b in zip(first, again))
+
+
 # ------------------------------------------- key-set backward and the ring ---
 
 def _stats_over(q, k, v, do, off, causal):
