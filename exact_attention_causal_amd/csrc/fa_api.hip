@@ -71,12 +71,9 @@ int map_launch(int rc) {
     return FA_EHIP;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S,
-           int D, float scale, int causal, int dtype, hipStream_t stream) {
+// Argument checks shared by fa_fwd and fa_fwd_ws (all before the device query).
+int check_fwd(const void *q, const void *k, const void *v, const void *o, const float *lse, int B, int H,
+              int S, int D, float scale, int causal, int dtype) {
     if (!q || !k || !v || !o || !lse) return FA_EINVAL;
     if (causal != 0 && causal != 1) return FA_EINVAL;
     if (int rc = check_scale(scale)) return rc;
@@ -86,6 +83,16 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     // one workgroup per 256 queries of every head must fit a launch grid (the
     // 512-query tile needs fewer; the 128-query one is chosen only for small grids)
     if ((long long)((S + 255) / 256) * B * H > 0x7fffffffLL) return FA_EINVAL;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S,
+           int D, float scale, int causal, int dtype, hipStream_t stream) {
+    if (int rc = check_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype)) return rc;
     const int ncu = fa::stream_cu_count(stream);
     if (ncu <= 0) return FA_EHIP;
     return map_launch(fa::launch_fwd(dtype, q, k, v, o, lse, B * H, S, D, scale, causal, ncu, stream));
@@ -102,14 +109,8 @@ size_t fa_fwd_workspace_size(int B, int H, int S, int D, int dtype) {
 int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
               size_t workspace_bytes, int B, int H, int S, int D, float scale, int causal, int dtype,
               hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse) return FA_EINVAL;
-    if (causal != 0 && causal != 1) return FA_EINVAL;
-    if (int rc = check_scale(scale)) return rc;
-    if (int rc = check_shape(B, H, S, D, dtype)) return rc;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-        return FA_EALIGN;
+    if (int rc = check_fwd(q, k, v, o, lse, B, H, S, D, scale, causal, dtype)) return rc;
     if (workspace && !aligned16(workspace)) return FA_EALIGN;
-    if ((long long)((S + 255) / 256) * B * H > 0x7fffffffLL) return FA_EINVAL;
     const int ncu = fa::stream_cu_count(stream);
     if (ncu <= 0) return FA_EHIP;
     const long long BH = (long long)B * H;
