@@ -88,6 +88,9 @@ def parse():
                     help="only time the benchmark sweep (B=1, H=1, S = 128 .. 65536 in powers of "
                          "two, D in 16/32/64/128, bf16 and fp32, causal and not), print a "
                          "markdown table and exit")
+    ap.add_argument("--shapes", action="store_true",
+                    help="only time forward and forward+backward (bf16, causal) on a list of common "
+                         "training shapes, print a markdown table and exit")
     ap.add_argument("--graph", action="store_true",
                     help="only time whole fwd+bwd steps launched one call at a time against the "
                          "same step captured once as a HIP graph and replayed, on the small "
@@ -376,6 +379,81 @@ def sweep(dev):
     return rows
 
 
+# common training shapes: (B, H, S, D)
+SHAPES = [(8, 32, 2048, 128), (4, 32, 4096, 128), (2, 32, 8192, 128), (1, 32, 16384, 128),
+          (1, 64, 8192, 128), (16, 16, 2048, 64), (8, 16, 4096, 64), (4, 40, 4096, 80),
+          (2, 24, 8192, 96), (1, 8, 32768, 128)]
+
+
+def shapes(dev):
+    """Forward and forward+backward throughput (bf16, causal) on common training shapes:
+    fwd = fa_fwd_ws (with the workspace its size query asks for), fwd+bwd = that +
+    fa_bwd_preprocess + fa_bwd; after about 100 ms of warm-up, the median over 5 batches of
+    back-to-back calls (HIP events around each batch)."""
+    from exact_attention_causal_amd.inputs import make_inputs
+    fa.load_library()
+    print("| B | H | S | D | fwd ms | fwd TFLOP/s (% of peak) | fwd+bwd ms | fwd+bwd TFLOP/s (% of peak) |")
+    print("|---|---|---|---|---|---|---|---|")
+    rows = []
+    for B, H, S, D in SHAPES:
+        code = fa.FA_BF16
+        q, k, v, do = (x.to(dev) for x in make_inputs(B, H, S, D, "bf16", seed=11))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, S), device=dev, dtype=torch.float32)
+        delta = torch.empty_like(lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = fa.fa_bwd_workspace_size(B, H, S, D, code)
+        ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
+        fws_bytes = fa.fa_fwd_workspace_size(B, H, S, D, code)
+        fws = torch.empty(max(fws_bytes, 1), device=dev, dtype=torch.uint8)
+        scale = 1.0 / math.sqrt(D)
+
+        def fwd():
+            rc = fa.fa_fwd_ws(q, k, v, o, lse, fws, fws_bytes, B, H, S, D, scale, 1, code)
+            assert rc == 0, fa.fa_strerror(rc)
+
+        def step():
+            fwd()
+            rc = fa.fa_bwd_preprocess(o, do, delta, B, H, S, D, code)
+            rc = rc or fa.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, ws, ws_bytes, B, H, S, D, scale, 1, code)
+            assert rc == 0, fa.fa_strerror(rc)
+
+        def timed(f):
+            # about 100 ms of warm-up (the clock settles), then the median over 5 batches of
+            # back-to-back calls, each batch about 20 ms
+            f()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            f()
+            torch.cuda.synchronize()
+            one = max(time.perf_counter() - t0, 1e-5)
+            for _ in range(int(0.1 / one) + 1):
+                f()
+            n = int(0.02 / one) + 1
+            ts = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(n):
+                    f()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) / n)
+            return statistics.median(ts)
+
+        t_f, t_s = timed(fwd), timed(step)
+        pairs = B * H * S * (S + 1) // 2
+        tf_f = 4 * D * pairs / (t_f * 1e-3) / 1e12
+        tf_s = 14 * D * pairs / (t_s * 1e-3) / 1e12
+        rows.append(dict(B=B, H=H, S=S, D=D, fwd_ms=round(t_f, 4), step_ms=round(t_s, 4)))
+        print(f"| {B} | {H} | {S} | {D} | {t_f:.3f} | {tf_f:.0f} ({100 * tf_f / PEAK_BF16:.1f} %) | "
+              f"{t_s:.3f} | {tf_s:.0f} ({100 * tf_s / PEAK_BF16:.1f} %) |", flush=True)
+        del q, k, v, do, o, lse, delta, dq, dk, dv, ws, fws
+        torch.cuda.empty_cache()
+    print(json.dumps({"shapes": rows}), flush=True)
+    return rows
+
+
 def graph_steps(dev):
     """Step time with the step's five kernels launched call by call (through the
     Python binding, as a Python caller does) against one replay of the same step
@@ -539,6 +617,9 @@ def main():
         return
     if args.graph:
         graph_steps(dev)
+        return
+    if args.shapes:
+        shapes(dev)
         return
     if args.hold > 0:
         hold(dev, WORKLOADS[args.workload], args.hold, args.hold_entry)
