@@ -3,10 +3,17 @@
 Each translation unit is compiled to an object in parallel, then linked into
 one shared library next to this file.  Run ``python -m
 exact_attention_causal_amd.build`` or call ``build()``.
+
+``python -m exact_attention_causal_amd.build --resources [substring]`` prints
+the compiler's resource report for every kernel of the device code instead
+(registers, spills, LDS per workgroup and the occupancy they allow), from the
+same flags; a substring keeps only the kernels whose names contain it.
 """
 import os
+import re
 import subprocess
 import sys
+import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,5 +67,99 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                     r"SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)")
+
+
+def kernel_label(sym: str) -> str:
+    """Readable name of one of this library's kernel symbols, e.g.
+    ``fwd_kernel<bf16, FwdTile<bf16, 128, 2, 32, 8, 1>, bf16, false>`` (the
+    function parameters are left out).  Template arguments are bf16 and float
+    types, integer and bool literals and class templates of namespace fa;
+    anything else returns the symbol as it is."""
+
+    def name(i):  # <length><identifier>
+        m = re.match(r"\d+", sym[i:])
+        n = int(m.group(0))
+        return sym[i + m.end():i + m.end() + n], i + m.end() + n
+
+    def args(i):  # I arg... E
+        out = []
+        i += 1
+        while sym[i] != "E":
+            if sym.startswith("DF16b", i):
+                out.append("bf16"); i += 5
+            elif sym[i] == "f":
+                out.append("float"); i += 1
+            elif sym[i] == "L":
+                m = re.match(r"L([ib])(n?)(\d+)E", sym[i:])
+                v = ("-" if m.group(2) else "") + m.group(3)
+                out.append(v if m.group(1) == "i" else ("true" if v == "1" else "false")); i += m.end()
+            elif sym.startswith("NS_", i):  # fa::Name<...> (nested name closed by a second E)
+                n, i = name(i + 3)
+                inner, i = args(i)
+                out.append(f"{n}<{', '.join(inner)}>")
+                if sym[i] != "E":
+                    raise ValueError(sym)
+                i += 1
+            else:
+                raise ValueError(sym)
+        return out, i + 1
+
+    try:
+        if not sym.startswith("_ZN2fa"):
+            return sym
+        n, i = name(6)
+        if i < len(sym) and sym[i] == "I":
+            a, _ = args(i)
+            return f"{n}<{', '.join(a)}>"
+        return n
+    except (ValueError, AttributeError, IndexError):
+        return sym
+
+
+def resources(pattern: str = ""):
+    """Per-kernel resource usage as the compiler reports it for these flags.
+
+    Returns dicts with the mangled and demangled name, VGPRs, AGPRs, spilled
+    registers, scratch bytes per lane, LDS bytes per workgroup and the waves
+    per SIMD (of 8) that registers and LDS allow.
+    """
+    rows = []
+    with tempfile.TemporaryDirectory() as tmp:
+        for src in SOURCES:
+            cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "--cuda-device-only", "-Rpass-analysis=kernel-resource-usage",
+                   "-c", os.path.join(CSRC, src), "-o", os.path.join(tmp, src + ".o")]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+            for line in r.stderr.splitlines():
+                m = _REMARK.search(line)
+                if not m:
+                    continue
+                key, val = m.groups()
+                if key == "Function Name":
+                    rows.append({"symbol": val, "source": src})
+                elif rows:
+                    rows[-1][key] = int(val)
+    out = []
+    for r in rows:
+        d = kernel_label(r["symbol"])
+        if pattern and pattern not in d and pattern not in r["symbol"]:
+            continue
+        out.append({"symbol": r["symbol"], "name": d, "source": r["source"], "vgprs": r.get("VGPRs"),
+                    "agprs": r.get("AGPRs"), "spills": r.get("VGPRs Spill", 0) + r.get("SGPRs Spill", 0),
+                    "scratch": r.get("ScratchSize [bytes/lane]"), "lds": r.get("LDS Size [bytes/block]"),
+                    "waves_per_simd": r.get("Occupancy [waves/SIMD]")})
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--resources" in sys.argv:
+        rest = [a for a in sys.argv[1:] if a != "--resources"]
+        print("waves/SIMD  VGPRs  AGPRs  spills  scratch  LDS bytes  kernel")
+        for r in resources(rest[0] if rest else ""):
+            print(f"{r['waves_per_simd']:>10}  {r['vgprs']:>5}  {r['agprs']:>5}  {r['spills']:>6}  {r['scratch']:>7}  "
+                  f"{r['lds']:>9}  {r['name']}")
+    else:
+        print(build(verbose="-v" in sys.argv))
