@@ -395,6 +395,12 @@ def _fwd_ws(q, k, v, causal, ws_bytes=None):
     (2, 1, 1000, 80, "f32", 1),     # 8 tiles: 8 chunks of 128 keys (16-row tails)
     (1, 2, 777, 32, "f32", 0),      # non-causal, ragged: 7 chunks
     (1, 4, 4096, 64, "f32", 1),     # 64 tiles at S >= 4096: 16 chunks
+    (1, 1, 4096, 16, "bf16", 1),    # 8 chunks, 16-row output tails
+    (1, 1, 4096, 80, "bf16", 1),    # 8 chunks, 16-row output tails
+    (1, 2, 3000, 96, "bf16", 1),    # 8 chunks of 384 keys
+    (1, 1, 2500, 32, "bf16", 0),    # non-causal: 8 chunks of 320 keys
+    (1, 1, 2048, 128, "f32", 1),    # 32 chunks of 64 keys (the fp32 D = 128 chunk tile)
+    (1, 2, 1500, 96, "f32", 1),     # 12 chunks of 128 keys
 ])
 def test_fwd_ws_split_matches_oracle(B, H, S, D, dtype, causal):
     code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
