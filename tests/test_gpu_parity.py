@@ -600,17 +600,17 @@ def test_random_shapes(case, dtype):
     check_full(q, k, v, do, dtype, causal=c["causal"], label=f"random {c}")
 
 
-@pytest.mark.parametrize("case", list(range(8)))
+@pytest.mark.parametrize("case", list(range(12)))
 def test_random_key_sets(case):
     """Seeded random query/key shard sizes and offsets through the key-set forward and backward:
     the shifted forward against the oracle, and the backward contributions against the oracle's
-    with the same L and Delta."""
+    with the same L and Delta.  The 12 cases take every head dimension in both dtypes."""
     rng = np.random.default_rng(1800 + case)
     dev = torch.device("cuda:0")
     Sq, Sk = int(rng.integers(1, 400)), int(rng.integers(1, 400))
     off = int(rng.integers(-Sq - 20, Sk + 20))
-    D = int(rng.choice([16, 64, 80, 128]))
-    dtype = "bf16" if case % 2 == 0 else "f32"
+    D = (16, 32, 64, 80, 96, 128)[case % 6]
+    dtype = "bf16" if case < 6 else "f32"
     causal = bool(rng.integers(0, 4))          # mostly causal
     q, _, _, do = make_inputs(1, 2, Sq, D, dtype, seed=1900 + case)
     _, k, v, _ = make_inputs(1, 2, Sk, D, dtype, seed=2000 + case)
