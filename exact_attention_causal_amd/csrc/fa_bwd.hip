@@ -1134,8 +1134,14 @@ static int delta_for(const void *o, const void *dout, float *delta, int BH, int 
 // shorter tiles to fit three stages in LDS.
 template <typename T, int D>
 using KvTileFor = KvTile<T, D, (sizeof(T) == 4 && D > 32) ? 32 : 64>;
+// (fp32 D = 128: Q^T, -dO^T and the dQ^T accumulator take 64 registers each,
+// so with two waves per SIMD the pass spilled 81 registers to scratch.  Four
+// waves per workgroup, one per SIMD, spill them into the accumulation
+// registers instead: the fp32 backward ran 25-33 % faster at D = 128, with
+// bit-identical results (each query's sum over key tiles keeps its order).
+// The same at D = 96 (7 spilled registers) was level.)
 template <typename T, int D>
-using QTileFor = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, 8>;
+using QTileFor = QTile<T, D, 1, (sizeof(T) == 4 && D > 80) ? 32 : 64, (sizeof(T) == 4 && D == 128) ? 4 : 8>;
 // (bf16 D = 128 keeps half of -V^T in LDS: with all of it in registers the
 // kernel spills; half in registers (254 VGPRs) reads half as much LDS per
 // block: the backward ran 1.3 % faster than with all of it in LDS.  Two 32-query blocks per
