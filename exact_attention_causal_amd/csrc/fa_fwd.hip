@@ -564,23 +564,31 @@ static bool pick(const FwdPlan &p, int &rc, const void *q, const void *k, const 
     return true;
 }
 
+// Waves of the shifted / split-key tile.
+template <typename T, int D>
+constexpr int fwd_gen_nw() { return (sizeof(T) == 4 && D == 128) ? 4 : 8; }
+
 template <typename T, int D, typename OutT, bool GEN>
 static int fwd_for(const void *q, const void *k, const void *v, OutT *o, float *lse, const FwdShape &a,
                    int n_split, int ncu, hipStream_t stream) {
-    using C1 = FwdTile<T, D, 1, fwd_bk<T, D>(), 8>;
-    // shifted / split keys: always the 256-query tile
-    if constexpr (GEN) return run_fwd<T, C1, OutT, GEN>(q, k, v, o, lse, a, n_split, stream);
-    const FwdPlan p = fwd_plan(sizeof(T) == 2 ? 1 : 0, a.BH, a.Sq, D, ncu);
-    FwdShape b = a;
-    b.band = p.band;
-    int rc = -5;
-    if constexpr (!GEN && sizeof(T) == 2 && D >= 64)
-        if (pick<T, FwdTile<T, D, 1, fwd_bk2<D>(), 8, 2>, OutT, GEN>(p, rc, q, k, v, o, lse, b, n_split, stream))
+    if constexpr (GEN) {
+        // shifted / split keys: always the 32-query-per-wave tile
+        return run_fwd<T, FwdTile<T, D, 1, fwd_bk<T, D>(), fwd_gen_nw<T, D>()>, OutT, GEN>(q, k, v, o, lse, a,
+                                                                                           n_split, stream);
+    } else {
+        const FwdPlan p = fwd_plan(sizeof(T) == 2 ? 1 : 0, a.BH, a.Sq, D, ncu);
+        FwdShape b = a;
+        b.band = p.band;
+        int rc = -5;
+        if constexpr (sizeof(T) == 2 && D >= 64)
+            if (pick<T, FwdTile<T, D, 1, fwd_bk2<D>(), 8, 2>, OutT, GEN>(p, rc, q, k, v, o, lse, b, n_split, stream))
+                return rc;
+        if constexpr (sizeof(T) == 2 && D == 128)
+            if (pick<T, FwdTile<T, D, 2, 32, 8>, OutT, GEN>(p, rc, q, k, v, o, lse, b, n_split, stream)) return rc;
+        if (pick<T, FwdTile<T, D, 1, fwd_bk<T, D>(), 8>, OutT, GEN>(p, rc, q, k, v, o, lse, b, n_split, stream))
             return rc;
-    if constexpr (!GEN && sizeof(T) == 2 && D == 128)
-        if (pick<T, FwdTile<T, D, 2, 32, 8>, OutT, GEN>(p, rc, q, k, v, o, lse, b, n_split, stream)) return rc;
-    if (pick<T, C1, OutT, GEN>(p, rc, q, k, v, o, lse, b, n_split, stream)) return rc;
-    return -5;  // (a plan with no matching tile: fwd_plan and the tiles disagree)
+        return -5;  // (a plan with no matching tile: fwd_plan and the tiles disagree)
+    }
 }
 
 template <typename T, bool GEN, typename OutT>
@@ -625,7 +633,7 @@ int launch_fwd_partial(int dtype, const void *q, const void *k, const void *v, f
                                                         FwdShape);
 #define FA_FWD_HEAD(T, D)                                                                        \
     FA_FWD_KERNEL(T, FwdTile<T COMMA D COMMA 1 COMMA fwd_bk<T COMMA D>() COMMA 8>, T, false)    \
-    FA_FWD_KERNEL(T, FwdTile<T COMMA D COMMA 1 COMMA fwd_bk<T COMMA D>() COMMA 8>, float, true)
+    FA_FWD_KERNEL(T, FwdTile<T COMMA D COMMA 1 COMMA fwd_bk<T COMMA D>() COMMA fwd_gen_nw<T COMMA D>()>, float, true)
 FA_FWD_HEAD(bf16, 16)
 FA_FWD_HEAD(bf16, 32)
 FA_FWD_HEAD(bf16, 64)
