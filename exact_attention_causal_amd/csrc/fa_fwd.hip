@@ -541,6 +541,18 @@ int fwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t max_p
         // bf16 (whose forward already runs two key groups when tiles are
         // few): only long walks over very few tiles gain, 1.1-2.3x
         if (S >= 2048 && 4 * tiles <= cu && 64 * tiles <= S) n = 8 * tiles <= cu ? 8 : 4;
+    } else if (D == 128) {
+        // fp32 D = 128, whose chunk tile has 128 queries (fwd_gen_nw): about
+        // one chunk tile per CU, fewer chunks past CU/4 tiles (each chunk's
+        // merge input grows with n).  Measured at B*H = 1..16, S = 2048..16384
+        // against every n up to the fp32 rule below: 4-44 % faster than it.
+        const long long t = (long long)BH * ((S + 127) / 128);
+        if (4 * t <= cu)
+            n = cu / t;
+        else if (2 * t <= cu)
+            n = 3;
+        else if (t <= 2 * cu && causal)
+            n = 2;
     } else {
         // fp32 (long steps, no two-group tile): 1.5-10x up to one tile per CU
         if (8 * tiles <= cu)

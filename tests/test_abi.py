@@ -132,13 +132,19 @@ def test_fwd_workspace_size(lib):
     # bf16, 48 tiles: 4 chunks
     assert fa.fa_fwd_workspace_size(1, 3, 4096, 64, fa.FA_BF16) == 4 * 3 * 4096 * 64 * 4 + 4 * 3 * 4096 * 4
     # fp32, 32 tiles: ceil(256/32) = 8 chunks; 64 tiles at S >= 4096: 16; 256 tiles: 2
-    assert fa.fa_fwd_workspace_size(1, 1, 8192, 128, fa.FA_F32) == 8 * 8192 * 128 * 4 + 8 * 8192 * 4
+    assert fa.fa_fwd_workspace_size(1, 1, 8192, 64, fa.FA_F32) == 8 * 8192 * 64 * 4 + 8 * 8192 * 4
     assert fa.fa_fwd_workspace_size(1, 4, 4096, 64, fa.FA_F32) == 16 * 4 * 4096 * 64 * 4 + 16 * 4 * 4096 * 4
     assert fa.fa_fwd_workspace_size(1, 16, 4096, 64, fa.FA_F32) == 2 * 16 * 4096 * 64 * 4 + 2 * 16 * 4096 * 4
     # fp32, one head of 512: ceil(256/2) = 128 wanted, at most S/64 = 8 chunks of 64 keys
     assert fa.fa_fwd_workspace_size(1, 1, 512, 64, fa.FA_F32) == 8 * 512 * 64 * 4 + 8 * 512 * 4
-    # at most 256 MiB of partials: one head of 32768, D = 128 wants 16 chunks (270 MB); 15 fit
-    assert fa.fa_fwd_workspace_size(1, 1, 32768, 128, fa.FA_F32) == 15 * 32768 * 128 * 4 + 15 * 32768 * 4
+    # fp32 D = 128 counts tiles of 128 queries: 16 tiles: 256/16 = 16 chunks; 64: 4; 128: 3;
+    # 256 (causal): 2
+    assert fa.fa_fwd_workspace_size(1, 1, 2048, 128, fa.FA_F32) == 16 * 2048 * 128 * 4 + 16 * 2048 * 4
+    assert fa.fa_fwd_workspace_size(1, 1, 8192, 128, fa.FA_F32) == 4 * 8192 * 128 * 4 + 4 * 8192 * 4
+    assert fa.fa_fwd_workspace_size(2, 4, 2048, 128, fa.FA_F32) == 3 * 8 * 2048 * 128 * 4 + 3 * 8 * 2048 * 4
+    assert fa.fa_fwd_workspace_size(1, 1, 32768, 128, fa.FA_F32) == 2 * 32768 * 128 * 4 + 2 * 32768 * 4
+    assert fa.fa_fwd_workspace_size(1, 1, 65536, 128, fa.FA_F32) == 2 * 65536 * 128 * 4 + 2 * 65536 * 4  # 512
+    assert fa.fa_fwd_workspace_size(1, 2, 65536, 128, fa.FA_F32) == 0   # 1024 tiles
     assert fa.fa_fwd_workspace_size(1, 1, 0, 64, fa.FA_BF16) == 0
     assert fa.fa_fwd_workspace_size(1, 1, 128, 72, fa.FA_BF16) == 0
 

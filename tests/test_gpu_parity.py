@@ -399,7 +399,7 @@ def _fwd_ws(q, k, v, causal, ws_bytes=None):
     (1, 1, 4096, 80, "bf16", 1),    # 8 chunks, 16-row output tails
     (1, 2, 3000, 96, "bf16", 1),    # 8 chunks of 384 keys
     (1, 1, 2500, 32, "bf16", 0),    # non-causal: 8 chunks of 320 keys
-    (1, 1, 2048, 128, "f32", 1),    # 32 chunks of 64 keys (the fp32 D = 128 chunk tile)
+    (1, 1, 2048, 128, "f32", 1),    # 16 chunks of 128 keys (the fp32 D = 128 chunk tile)
     (1, 2, 1500, 96, "f32", 1),     # 12 chunks of 128 keys
 ])
 def test_fwd_ws_split_matches_oracle(B, H, S, D, dtype, causal):
