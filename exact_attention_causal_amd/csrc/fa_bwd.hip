@@ -1260,7 +1260,15 @@ BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_byt
         // while the walk is long (S >= 32 tiles), 4 up to half, 2 up to two
         // per CU -- within 5 % of the best count at every measured point.
         const long long t = (long long)BH * ((S + 127) / 128);
-        n = (4 * t <= cu || 32 * t <= S) ? 8 : 2 * t <= cu ? 4 : t <= 2 * cu ? 2 : 1;
+        if (D == 128)
+            // (D = 128: the dQ pass runs 4-wave, 128-query workgroups, twice as
+            // many per chunk.  Over B*H = 1..32, S = 1024..16384 against every
+            // count up to the rule below: 8 chunks up to an eighth workgroup per
+            // CU, 4 up to a quarter, 3 up to half, 2 up to two; 3-39 % faster
+            // where it differs.)
+            n = 8 * t <= cu ? 8 : 4 * t <= cu ? 4 : 2 * t <= cu ? 3 : t <= 2 * cu ? 2 : 1;
+        else
+            n = (4 * t <= cu || 32 * t <= S) ? 8 : 2 * t <= cu ? 4 : t <= 2 * cu ? 2 : 1;
     }
     // at most 8 chunks (16 were no faster overall and hold twice the
     // partials), and no more partial results than the budget

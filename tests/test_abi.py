@@ -65,8 +65,9 @@ def test_workspace_size(lib):
     assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_BF16) == 8192 * 4 + 3 * 8 * 8192 * 128 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 65536, 128, fa.FA_BF16) == 65536 * 4 + 3 * 2 * 65536 * 128 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 1000, 80, fa.FA_BF16) == 4096 + 3 * 8 * 1000 * 80 * 4
-    # fp32: 128-key dK/dV workgroups, split more readily (64 tiles: 8 chunks)
-    assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_F32) == 8192 * 4 + 3 * 8 * 8192 * 128 * 4
+    # fp32: 128-key dK/dV workgroups, split more readily (64 tiles: 8 chunks at D = 64, 4 at D = 128)
+    assert fa.fa_bwd_workspace_size(1, 1, 8192, 64, fa.FA_F32) == 8192 * 4 + 3 * 8 * 8192 * 64 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 8192, 128, fa.FA_F32) == 8192 * 4 + 3 * 4 * 8192 * 128 * 4
     assert fa.fa_bwd_workspace_size(4, 32, 8192, 128, fa.FA_F32) == 128 * 8192 * 4  # 8192 tiles
     assert fa.fa_bwd_workspace_size(2, 16, 8192, 128, fa.FA_BF16) == 32 * 8192 * 4   # enough tiles
 
@@ -302,6 +303,13 @@ def test_plan_thresholds_follow_the_cu_count(lib):
     assert _plan(1, 32, 1024, 64, f32, 256).bwd_chunks == 2     # t = 256
     assert _plan(1, 4, 8192, 64, f32, 256).bwd_chunks == 8      # t = 256 <= S/32
     assert _plan(1, 32, 4096, 64, f32, 256).bwd_chunks == 1     # t = 1024
+    # fp32 D = 128 (4-wave dQ workgroups): 8 up to CU/8, 4 up to CU/4, 3 up to CU/2, 2 up to 2 CU
+    assert _plan(1, 1, 4096, 128, f32, 256).bwd_chunks == 8     # t = 32
+    assert _plan(1, 1, 8192, 128, f32, 256).bwd_chunks == 4     # t = 64
+    assert _plan(2, 4, 2048, 128, f32, 256).bwd_chunks == 3     # t = 128
+    assert _plan(1, 4, 8192, 128, f32, 256).bwd_chunks == 2     # t = 256 (S/32 no longer counts)
+    assert _plan(1, 8, 8192, 128, f32, 256).bwd_chunks == 2     # t = 512
+    assert _plan(1, 16, 8192, 128, f32, 256).bwd_chunks == 1    # t = 1024
     # split backward: below one dK/dV tile of 256 keys per CU, n = ceil(CU / tiles) <= 8 chunks;
     # one to two tiles per CU: 2 chunks from S = 4096 on; S <= 512: 4 chunks below CU/16 tiles
     p = _plan(1, 1, 8192, 128, bf, 256)          # 32 tiles: 8 wanted

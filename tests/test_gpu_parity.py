@@ -856,6 +856,17 @@ def test_plan_uses_the_device_cu_count():
     assert rc2 == 0 and explicit.as_dict() == plan.as_dict()
 
 
+@pytest.mark.parametrize("B,H,S,chunks", [(2, 4, 2048, 3), (1, 1, 3000, 8)])
+def test_fp32_split_backward_d128(B, H, S, chunks):
+    # fp32 D = 128: the dQ pass on 4-wave workgroups, split over key chunks (3: a chunk count
+    # that does not divide the tiles), the pair dK/dV kernel over query chunks
+    D = 128
+    rc, plan = fa.fa_get_plan(B, H, S, D, fa.FA_F32, 0)
+    assert rc == 0 and plan.bwd_chunks == chunks, plan.as_dict()
+    q, k, v, do = make_inputs(B, H, S, D, "f32", seed=815 + S)
+    check_full(q, k, v, do, "f32", causal=True, label=f"fp32 D=128 split backward B={B} H={H} S={S}")
+
+
 def test_fp32_split_backward_one_head():
     # one fp32 head: the pair dK/dV kernel over 8 query chunks and dQ over 8 key chunks (ragged
     # last chunk), fp32 partials summed; element by element against the oracle at 1e-4
