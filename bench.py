@@ -91,6 +91,10 @@ def parse():
     ap.add_argument("--shapes", action="store_true",
                     help="only time forward and forward+backward (bf16, causal) on a list of common "
                          "training shapes, print a markdown table and exit")
+    ap.add_argument("--peak", action="store_true",
+                    help="only run the matrix-core microbenchmark (libfa_peak.so): bf16 32x32x16 and "
+                         "fp32 32x32x2 MFMA loops with no memory traffic, on zero, constant and "
+                         "random operands; print one JSON line per case and exit")
     ap.add_argument("--graph", action="store_true",
                     help="only time whole fwd+bwd steps launched one call at a time against the "
                          "same step captured once as a HIP graph and replayed, on the small "
@@ -589,6 +593,44 @@ def vs_materialised(dev):
             torch.cuda.empty_cache()
 
 
+PUBLISHED_PEAK = {"bf16": 2516.6, "fp32": 157.3}   # dense MFMA TFLOP/s, 2.4 GHz
+
+
+def peak(dev):
+    """Matrix-core throughput with no memory traffic: per dtype and operand kind, the mean
+    over 10 launches after 5 warm-up launches (HIP events on the launching stream)."""
+    import ctypes
+    from exact_attention_causal_amd import build as fab
+    if not os.path.exists(fab.PEAK_LIB):
+        raise RuntimeError(f"{fab.PEAK_LIB} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(fab.PEAK_LIB)
+    lib.fa_peak_mfma.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_peak_mfma.restype = ctypes.c_int
+    lib.fa_peak_mfma_flop.argtypes = [ctypes.c_int] * 3
+    lib.fa_peak_mfma_flop.restype = ctypes.c_double
+    # (launches of 4-19 ms; 16384 bf16 workgroups keep the last round of waves short)
+    out = torch.empty(16384 * 256, device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    for name, code, blocks, iters in (("bf16", 1, 16384, 1024), ("fp32", 0, 4096, 512)):
+        for mode, operands in enumerate(("zeros", "constant", "random N(0,1)")):
+            launch = lambda: lib.fa_peak_mfma(code, mode, blocks, iters, out.data_ptr(), stream.cuda_stream)
+            for _ in range(5):
+                assert launch() == 0
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(10):
+                assert launch() == 0
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 10
+            tf = lib.fa_peak_mfma_flop(code, blocks, iters) / (ms * 1e-3) / 1e12
+            print(json.dumps({"peak": f"mfma {name} " + ("32x32x16" if code == 1 else "32x32x2"),
+                              "operands": operands, "blocks": blocks, "iters": iters, "ms": round(ms, 4),
+                              "tflops": round(tf, 1),
+                              "published": PUBLISHED_PEAK[name], "frac": round(tf / PUBLISHED_PEAK[name], 4)}),
+                  flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -617,6 +659,9 @@ def main():
         return
     if args.graph:
         graph_steps(dev)
+        return
+    if args.peak:
+        peak(dev)
         return
     if args.shapes:
         shapes(dev)

@@ -1,7 +1,9 @@
 """Build the gfx950 HIP library (libfa_mi355x.so) in-tree with hipcc.
 
 Each translation unit is compiled to an object in parallel, then linked into
-one shared library next to this file.  Run ``python -m
+one shared library next to this file.  The matrix-core microbenchmark that
+``bench.py --peak`` runs is built beside it as libfa_peak.so; nothing in the
+attention library loads it.  Run ``python -m
 exact_attention_causal_amd.build`` or call ``build()``.
 
 ``python -m exact_attention_causal_amd.build --resources [substring]`` prints
@@ -21,6 +23,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa_mi355x.so")
+# the matrix-core microbenchmark (bench.py --peak), a library of its own
+PEAK_LIB = os.path.join(HERE, "libfa_peak.so")
+PEAK_SOURCE = "peak.hip"
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_merge.hip"]
 
@@ -64,6 +69,14 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    tmp = PEAK_LIB + ".tmp"
+    cmd = [HIPCC, *CFLAGS, "-shared", os.path.join(CSRC, PEAK_SOURCE), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PEAK_SOURCE}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PEAK_LIB)
     return LIB
 
 

@@ -43,3 +43,23 @@ def test_resource_report_of_one_source(monkeypatch):
         assert 1 <= r["waves_per_simd"] <= 8
     only = build.resources("merge_kernel<bf16, 128>")
     assert [r["name"] for r in only] == ["merge_kernel<bf16, 128>"]
+
+
+def test_peak_library_rejects_bad_arguments():
+    # the matrix-core microbenchmark library (bench.py --peak): argument checks and the FLOP
+    # count, no launch
+    import ctypes
+    if not os.path.exists(build.PEAK_LIB):
+        pytest.fail("libfa_peak.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(build.PEAK_LIB)
+    lib.fa_peak_mfma.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_peak_mfma_flop.argtypes = [ctypes.c_int] * 3
+    lib.fa_peak_mfma_flop.restype = ctypes.c_double
+    out = 0x100000
+    for dtype, mode, blocks, iters, ptr in [(2, 0, 1, 1, out), (1, 3, 1, 1, out), (1, 0, 0, 1, out),
+                                            (1, 0, 1, 0, out), (0, 0, 1, 1, None), (1, 0, (1 << 22) + 1, 1, out)]:
+        assert lib.fa_peak_mfma(dtype, mode, blocks, iters, ptr, None) == -1
+    # 4 waves x 16 instructions per round: 32768 FLOP each (bf16 32x32x16), 4096 (fp32 32x32x2)
+    assert lib.fa_peak_mfma_flop(1, 3, 5) == 3 * 4 * 5 * 16 * 32768
+    assert lib.fa_peak_mfma_flop(0, 3, 5) == 3 * 4 * 5 * 16 * 4096
+    assert lib.fa_peak_mfma_flop(2, 3, 5) == 0
