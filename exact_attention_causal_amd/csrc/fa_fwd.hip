@@ -544,14 +544,18 @@ int fwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t max_p
     } else if (D == 128) {
         // fp32 D = 128, whose chunk tile has 128 queries (fwd_gen_nw): about
         // one chunk tile per CU, fewer chunks past CU/4 tiles (each chunk's
-        // merge input grows with n).  Measured at B*H = 1..16, S = 2048..16384
-        // against every n up to the fp32 rule below: 4-44 % faster than it.
+        // merge input grows with n).  Measured at B*H = 1..16, S = 2048..32768
+        // against every n up to 16, causal and not: 4-44 % faster than the
+        // rule below, and within 3 % of the best count except at one point
+        // (one causal head at S = 8192: 16 chunks 11 % faster).  Without the
+        // mask every tile walks all keys: 3 chunks would leave half a round
+        // of tiles, and past CU tiles the plain forward already fills the GPU.
         const long long t = (long long)BH * ((S + 127) / 128);
         if (4 * t <= cu)
             n = cu / t;
         else if (2 * t <= cu)
-            n = 3;
-        else if (t <= 2 * cu && causal)
+            n = causal ? 3 : 2;
+        else if (t <= (causal ? 2 * cu : cu))
             n = 2;
     } else {
         // fp32 (long steps, no two-group tile): 1.5-10x up to one tile per CU
