@@ -1233,7 +1233,7 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
 
 BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_bytes) {
     BwdSplit r{1, S};
-    if ((dtype != 0 && dtype != 1) || !head_dim_supported(D) || S <= 256) return r;
+    if ((dtype != 0 && dtype != 1) || !head_dim_supported(D) || S <= (dtype == 0 ? 64 : 256)) return r;  // (>= 2 chunks of 64)
     const long long cu = ncu > 0 ? ncu : 1;
     // The longest causal dK/dV workgroup walks the whole sequence.  Splitting
     // shortens that walk n-fold but writes and sums n sets of fp32 partials.
@@ -1269,6 +1269,10 @@ BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_byt
             n = 8 * t <= cu ? 8 : 4 * t <= cu ? 4 : 2 * t <= cu ? 3 : t <= 2 * cu ? 2 : 1;
         else
             n = (4 * t <= cu || 32 * t <= S) ? 8 : 2 * t <= cu ? 4 : t <= 2 * cu ? 2 : 1;
+        // S <= 256 (one or two tiles per head; bf16 does not split there):
+        // 1.3-2.4x faster up to CU/2 tiles (B*H = 1..16, D = 32..128), 10 %
+        // slower at one tile per CU (B*H = 128, S = 256, 2 chunks)
+        if (S <= 256 && 2 * t > cu) n = 1;
     }
     // at most 8 chunks (16 were no faster overall and hold twice the
     // partials), and no more partial results than the budget

@@ -310,6 +310,13 @@ def test_plan_thresholds_follow_the_cu_count(lib):
     assert _plan(1, 4, 8192, 128, f32, 256).bwd_chunks == 2     # t = 256 (S/32 no longer counts)
     assert _plan(1, 8, 8192, 128, f32, 256).bwd_chunks == 2     # t = 512
     assert _plan(1, 16, 8192, 128, f32, 256).bwd_chunks == 1    # t = 1024
+    # fp32 at S <= 256: chunks of 64 rows up to CU/2 tiles, none from S <= 64 or past CU/2
+    p = _plan(1, 1, 200, 80, f32, 256)
+    assert (p.bwd_chunks, p.bwd_chunk_rows) == (4, 64)
+    assert _plan(4, 16, 256, 64, f32, 256).bwd_chunks == 4      # t = 128
+    assert _plan(8, 16, 256, 64, f32, 256).bwd_chunks == 1      # t = 256
+    assert _plan(1, 1, 64, 64, f32, 256).bwd_chunks == 1
+    assert _plan(1, 1, 256, 64, bf, 256).bwd_chunks == 1        # bf16: S <= 256 never splits
     # split backward: below one dK/dV tile of 256 keys per CU, n = ceil(CU / tiles) <= 8 chunks;
     # one to two tiles per CU: 2 chunks from S = 4096 on; S <= 512: 4 chunks below CU/16 tiles
     p = _plan(1, 1, 8192, 128, bf, 256)          # 32 tiles: 8 wanted

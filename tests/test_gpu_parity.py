@@ -868,6 +868,16 @@ def test_fp32_split_backward_d128(B, H, S, chunks):
     check_full(q, k, v, do, "f32", causal=True, label=f"fp32 D=128 split backward B={B} H={H} S={S}")
 
 
+@pytest.mark.parametrize("B,H,S,D,chunks", [(1, 1, 200, 80, 4), (1, 2, 97, 64, 2), (2, 3, 256, 128, 4)])
+def test_fp32_split_backward_short(B, H, S, D, chunks):
+    # fp32 at S <= 256: chunks of 64 rows (a ragged last one), causal and not
+    rc, plan = fa.fa_get_plan(B, H, S, D, fa.FA_F32, 0)
+    assert rc == 0 and plan.bwd_chunks == chunks, plan.as_dict()
+    q, k, v, do = make_inputs(B, H, S, D, "f32", seed=840 + S)
+    for causal in (True, False):
+        check_full(q, k, v, do, "f32", causal=causal, label=f"fp32 short split B={B} H={H} S={S} D={D} {causal}")
+
+
 def test_fp32_split_backward_one_head():
     # one fp32 head: the pair dK/dV kernel over 8 query chunks and dQ over 8 key chunks (ragged
     # last chunk), fp32 partials summed; element by element against the oracle at 1e-4

@@ -66,7 +66,7 @@ def test_noalloc_matches_fa_bwd_on_consecutive_calls():
     # split backward (8 chunks fit the scratch), then a smaller problem (3 chunks)
     run(1, 2, 1500, 128, "bf16", seed=701, with_oracle=True)
     run(1, 1, 300, 64, "bf16", seed=702, with_oracle=True)
-    # fp32 (split into 6 chunks), then smaller again (unsplit)
+    # fp32 (split into 6 chunks), then smaller again (2 chunks, the second of one row)
     run(2, 2, 333, 80, "f32", seed=703, with_oracle=True)
     run(1, 1, 65, 32, "f32", seed=704, with_oracle=True)
 
