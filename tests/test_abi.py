@@ -132,6 +132,13 @@ def test_fwd_workspace_size(lib):
     assert fa.fa_fwd_workspace_size(1, 1, 4096, 128, fa.FA_BF16) == 8 * 4096 * 128 * 4 + 8 * 4096 * 4
     # bf16, 48 tiles: 4 chunks
     assert fa.fa_fwd_workspace_size(1, 3, 4096, 64, fa.FA_BF16) == 4 * 3 * 4096 * 64 * 4 + 4 * 3 * 4096 * 4
+    # bf16 D <= 32 (no two-group tile), S >= 4096: 6 (causal) chunks up to one tile per CU, and up
+    # to two from S = 16384 on
+    for B, H, S, D in [(1, 1, 32768, 16), (1, 4, 8192, 32), (1, 16, 4096, 16), (1, 8, 16384, 32)]:
+        assert fa.fa_fwd_workspace_size(B, H, S, D, fa.FA_BF16) == 6 * B * H * S * D * 4 + 6 * B * H * S * 4
+    assert fa.fa_fwd_workspace_size(1, 32, 2048, 16, fa.FA_BF16) == 0    # S < 4096
+    assert fa.fa_fwd_workspace_size(1, 16, 8192, 32, fa.FA_BF16) == 0    # 512 tiles, S < 16384
+    assert fa.fa_fwd_workspace_size(1, 4, 8192, 64, fa.FA_BF16) == 0     # D = 64: two key groups instead
     # fp32, 32 tiles: ceil(256/32) = 8 chunks; 64 tiles at S >= 4096: 16; 256 tiles: 2
     assert fa.fa_fwd_workspace_size(1, 1, 8192, 64, fa.FA_F32) == 8 * 8192 * 64 * 4 + 8 * 8192 * 4
     assert fa.fa_fwd_workspace_size(1, 4, 4096, 64, fa.FA_F32) == 16 * 4 * 4096 * 64 * 4 + 16 * 4 * 4096 * 4

@@ -402,6 +402,10 @@ def _fwd_ws(q, k, v, causal, ws_bytes=None):
     (1, 1, 2048, 128, "f32", 1),    # 16 chunks of 128 keys (the fp32 D = 128 chunk tile)
     (1, 2, 1500, 96, "f32", 1),     # 12 chunks of 128 keys
     (1, 4, 8192, 128, "f32", 0),    # non-causal, 256 tiles of 128 queries: 2 chunks
+    (1, 4, 8192, 32, "bf16", 1),    # D <= 32, 128 tiles: 6 chunks
+    (1, 2, 6000, 16, "bf16", 0),    # D <= 32 non-causal, ragged, 48 tiles: 4 chunks
+    (1, 5, 16400, 32, "bf16", 0),   # D <= 32 non-causal, ragged, 325 tiles, S >= 16384: 2 chunks
+    (1, 10, 5000, 16, "bf16", 1),   # D <= 32, ragged, 200 tiles: 6 chunks
 ])
 def test_fwd_ws_split_matches_oracle(B, H, S, D, dtype, causal):
     code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
