@@ -42,8 +42,8 @@ EXTRA_WORKLOADS = ("bf16_b1h32_s16000_d80",)
 # by a hash of every source the forward kernel and its launch plan compile
 # from: once one changes, the figure is stale and reported as null until the
 # counters are taken again.
-FWD_TRAFFIC = {"sources_sha1": "7ba4f3a31eb08f3bb6ea3b4bf48eaa6d70f1e148",
-               "bytes": {"bf16_b1h16_s65536_d128": 4668832256, "bf16_b1h32_s16000_d80": 2117122624}}
+FWD_TRAFFIC = {"sources_sha1": "58e6b6daff82c533b5f5349243e13f37e9d304e2",
+               "bytes": {"bf16_b1h16_s65536_d128": 4668831264, "bf16_b1h32_s16000_d80": 2119712512}}
 FWD_SOURCES = ("exact_attention_causal_amd/csrc/fa_fwd.hip", "exact_attention_causal_amd/csrc/fa_common.hpp",
                "exact_attention_causal_amd/csrc/fa_launch.hpp")
 
@@ -289,7 +289,7 @@ def sweep(dev):
     """Latency sweep over the grid of the handout's FlashAttention-2 benchmark.
 
     One head (B=1, H=1) per point, as in that benchmark; times are medians of
-    HIP-event times over repeated calls after warm-up.  fwd = fa_fwd_ws (fa_fwd
+    HIP-event times over repeated calls after about 20 ms of warm-up calls.  fwd = fa_fwd_ws (fa_fwd
     with the workspace its size query asks for: it splits the keys of few-tile
     problems); fwd+bwd = that + fa_bwd_preprocess + fa_bwd.
     """
@@ -332,8 +332,15 @@ def sweep(dev):
                         assert rc == 0, fa.fa_strerror(rc)
 
                     def timed(f, n):
-                        for _ in range(3):
+                        # warm-up: at least 3 calls and about 20 ms of them, so the
+                        # GPU holds its working clock before the timed calls
+                        t0, calls = time.perf_counter(), 0
+                        while calls < 3 or time.perf_counter() - t0 < 0.02:
                             f()
+                            calls += 1
+                            if calls % 8 == 0:
+                                torch.cuda.synchronize()
+                        torch.cuda.synchronize()
                         ts = []
                         for _ in range(n):
                             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

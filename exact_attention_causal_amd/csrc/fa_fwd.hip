@@ -577,7 +577,11 @@ int fwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t max_p
         else if (2 * tiles <= cu)
             n = S >= 4096 ? 16 : 4;
         else if (tiles <= cu && causal)
-            n = 2;  // (the causal imbalance of one tile per CU; level or slower without it)
+            // (the causal imbalance of one tile per CU; level or slower
+            // without the mask.  D >= 64: 2 chunks 1.5-1.6x faster, within
+            // 10 % of the best count; D = 16 and 32 gain little from 2
+            // (0.96-1.0) but 1.1-1.7x from 8 (B*H = 1..32, S = 2048..65536))
+            n = D <= 32 ? 8 : 2;
     }
     n = std::min<long long>(n, std::min<long long>(32, S / 64));  // chunks of 64 keys or more
     while (n > 1 && fwd_part_bytes((int)n, BH, S, D) > max_part_bytes) --n;

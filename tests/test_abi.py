@@ -143,6 +143,7 @@ def test_fwd_workspace_size(lib):
     assert fa.fa_fwd_workspace_size(1, 1, 8192, 64, fa.FA_F32) == 8 * 8192 * 64 * 4 + 8 * 8192 * 4
     assert fa.fa_fwd_workspace_size(1, 4, 4096, 64, fa.FA_F32) == 16 * 4 * 4096 * 64 * 4 + 16 * 4 * 4096 * 4
     assert fa.fa_fwd_workspace_size(1, 16, 4096, 64, fa.FA_F32) == 2 * 16 * 4096 * 64 * 4 + 2 * 16 * 4096 * 4
+    assert fa.fa_fwd_workspace_size(1, 16, 4096, 32, fa.FA_F32) == 8 * 16 * 4096 * 32 * 4 + 8 * 16 * 4096 * 4  # D <= 32
     # fp32, one head of 512: ceil(256/2) = 128 wanted, at most S/64 = 8 chunks of 64 keys
     assert fa.fa_fwd_workspace_size(1, 1, 512, 64, fa.FA_F32) == 8 * 512 * 64 * 4 + 8 * 512 * 4
     # fp32 D = 128 counts tiles of 128 queries: 16 tiles: 256/16 = 16 chunks; 64: 4; 128: 3;
