@@ -338,6 +338,12 @@ def test_plan_thresholds_follow_the_cu_count(lib):
     p = _plan(1, 1, 512, 64, bf, 256)            # S <= 512, 2 tiles: 4 chunks of 128 rows
     assert (p.bwd_chunks, p.bwd_chunk_rows) == (4, 128)
     assert _plan(4, 12, 512, 64, bf, 256).bwd_chunks == 1   # S <= 512, 96 tiles: the partials cost more
+    assert _plan(1, 2, 16384, 64, bf, 256).bwd_chunks == 3  # CU/2 tiles, S >= 4096: at least 3 chunks
+    assert _plan(1, 32, 1024, 64, bf, 256).bwd_chunks == 2  # CU/2 tiles, S < 4096: ceil(CU / tiles)
+    assert _plan(1, 3, 16384, 128, bf, 256).bwd_chunks == 2  # 192 tiles: 2
+    assert _plan(1, 4, 16384, 16, bf, 256).bwd_chunks == 8  # D = 16 (two workgroups per CU), S >= 4096
+    assert _plan(1, 32, 2048, 16, bf, 256).bwd_chunks == 3  # D = 16, S < 4096
+    assert _plan(2, 32, 4096, 16, bf, 256).bwd_chunks == 1  # D = 16, 1024 tiles
     p = _plan(1, 1, 65536, 128, bf, 256)         # 256 tiles: 2 wanted, 2 fit in 256 MiB
     assert (p.bwd_chunks, p.bwd_chunk_rows) == (2, 32768)
     assert _plan(1, 1, 65536, 128, bf, 128).bwd_chunks == 1
