@@ -145,7 +145,7 @@ size_t fa_bwd_workspace_size(int B, int H, int S, int D, int dtype) {
     // each chunk of the split backward, for the current device's CU count
     int ncu = fa::stream_cu_count(nullptr);
     if (ncu <= 0) ncu = kAssumedCU;
-    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, ncu, fa::kMaxSplitBytes);
+    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, 1, ncu, fa::kMaxSplitBytes);  // (causal: the most chunks)
     return fa::bwd_lse2_bytes(BH * S) + fa::bwd_part_bytes(sp, BH, S, D);
 }
 
@@ -178,7 +178,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *dout, const 
     if (ncu <= 0) return FA_EHIP;
     // the split backward takes as many chunks as the workspace holds partials for
     const size_t budget = workspace_bytes - base < fa::kMaxSplitBytes ? workspace_bytes - base : fa::kMaxSplitBytes;
-    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, ncu, budget);
+    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, causal, ncu, budget);
     return map_launch(fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv,
                                      static_cast<float *>(workspace), (int)BH, S, D, scale, causal, sp, stream));
 }
@@ -194,7 +194,7 @@ int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *dout
     if (ncu <= 0) return FA_EHIP;
     float *scratch = fa::noalloc_scratch(stream);
     if (!scratch) return FA_EHIP;
-    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, ncu, fa::kNoAllocScratchBytes - base);
+    const fa::BwdSplit sp = fa::bwd_split(dtype, (int)BH, S, D, causal, ncu, fa::kNoAllocScratchBytes - base);
     return map_launch(fa::launch_bwd(dtype, q, k, v, dout, lse, delta, dq, dk, dv, scratch, (int)BH, S, D,
                                      scale, causal, sp, stream));
 }
@@ -208,7 +208,7 @@ int fa_get_plan(int B, int H, int S, int D, int dtype, int num_cu, fa_plan *plan
     }
     const int BH = B * H;
     const fa::FwdPlan f = fa::fwd_plan(dtype, BH, S, D, num_cu);
-    const fa::BwdSplit sp = fa::bwd_split(dtype, BH, S, D, num_cu, fa::kMaxSplitBytes);
+    const fa::BwdSplit sp = fa::bwd_split(dtype, BH, S, D, 1, num_cu, fa::kMaxSplitBytes);
     plan->num_cu = num_cu;
     plan->fwd_block_queries = f.bq;
     plan->fwd_key_groups = f.groups;

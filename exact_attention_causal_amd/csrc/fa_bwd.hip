@@ -1231,7 +1231,7 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
     return -2;
 }
 
-BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_bytes) {
+BwdSplit bwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t max_part_bytes) {
     BwdSplit r{1, S};
     if ((dtype != 0 && dtype != 1) || !head_dim_supported(D) || S <= (dtype == 0 ? 64 : 256)) return r;  // (>= 2 chunks of 64)
     const long long cu = ncu > 0 ? ncu : 1;
@@ -1252,12 +1252,13 @@ BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_byt
             // D = 16 fits two workgroups per CU, placed together as the launch
             // starts: finer chunks keep two long causal walks off one CU
             // (B*H = 1..32, S = 2048..65536: 1.3-1.8x faster than 2 chunks)
-            n = S >= 4096 ? 8 : 3;
+            n = std::max<long long>(S >= 4096 ? 8 : 3, (cu + tiles - 1) / tiles);
         else if (2 * tiles <= cu)
-            // (from S = 4096 on at least 3: with 2, half of the first chunk's
-            // key tiles see no query of it; 3 chunks were 12-27 % faster at
-            // CU/2 tiles, D = 32..128, but 13 % slower at S = 1024)
-            n = std::max<long long>(S >= 4096 ? 3 : 1, (cu + tiles - 1) / tiles);
+            // (causal, from S = 4096 on, at least 3: with 2, half of the first
+            // chunk's key tiles see no query of it; 3 chunks were 12-27 %
+            // faster at CU/2 tiles, D = 32..128, but 13 % slower at S = 1024
+            // and 13-20 % slower without the mask)
+            n = std::max<long long>(causal && S >= 4096 ? 3 : 1, (cu + tiles - 1) / tiles);
         else if (tiles < cu)
             n = 2;
         else if (tiles < 2 * cu && S >= 4096)

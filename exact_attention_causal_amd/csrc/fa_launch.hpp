@@ -67,12 +67,14 @@ int launch_delta(int dtype, const void *o, const void *dout, float *delta, int B
 
 // How the backward of a problem with few key tiles per CU is split: n
 // chunks of `chunk` rows per pass (n = 1: not split), with at most
-// `max_part_bytes` of fp32 partial results.
+// `max_part_bytes` of fp32 partial results.  A causal problem never takes
+// fewer chunks than the same problem without the mask, so size queries,
+// which do not know the mask, ask with causal = 1.
 struct BwdSplit {
     int n, chunk;
 };
 constexpr size_t kMaxSplitBytes = (size_t)256 << 20;  // partials of the caller-workspace backward
-BwdSplit bwd_split(int dtype, int BH, int S, int D, int ncu, size_t max_part_bytes);
+BwdSplit bwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t max_part_bytes);
 
 // Bytes of the base-2 copy of lse at the start of the backward workspace (one
 // fp32 per row, rounded up to 256 bytes); the split's partials follow it.

@@ -124,13 +124,15 @@ int fa_bwd_preprocess(const void *o, const void *dout, float *delta,
  * (rounded up to 256 bytes), where fa_bwd keeps lse in base 2 (L * log2 e)
  * so that recomputing P = 2^(S * scale * log2 e - L * log2 e) costs no
  * multiply per probability.  For problems with too few key tiles to fill
- * the GPU (S > 256; the chunk count follows the number of dK/dV workgroups
- * per compute unit and S, as fa_get_plan reports it), fa_bwd can instead cut
- * each pass into n chunks (n <= 8, 64-row multiples) that run side by side
- * and sum their fp32 partial dQ, dK, dV in a fixed order (still
- * bit-reproducible): the size returned then adds 3*n*B*H*S*D fp32 values
- * (at most 256 MiB).  The compute-unit count is the current device's (that
- * of one MI355X, 256, when no device is visible).
+ * the GPU (S > 256 for bf16, S > 64 for fp32; the chunk count follows the
+ * number of dK/dV workgroups per compute unit, S, D and the mask, as
+ * fa_get_plan reports it), fa_bwd can instead cut each pass into n chunks
+ * (n <= 8, 64-row multiples) that run side by side and sum their fp32
+ * partial dQ, dK, dV in a fixed order (still bit-reproducible): the size
+ * returned then adds 3*n*B*H*S*D fp32 values (at most 256 MiB).  The size
+ * is that of the causal problem, which never takes fewer chunks than the
+ * same problem without the mask.  The compute-unit count is the current
+ * device's (that of one MI355X, 256, when no device is visible).
  * Returns 0 for invalid sizes; fa_bwd reports those.
  */
 size_t fa_bwd_workspace_size(int B, int H, int S, int D, int dtype);
@@ -260,8 +262,9 @@ typedef struct {
                                consecutive heads; b > 0 = each of the 8 XCDs takes every
                                8th head, in bands of b query tiles per head (B*H a
                                multiple of 8) */
-    int bwd_chunks;         /* chunks of the split backward (1: not split), with a
-                               workspace of fa_bwd_workspace_size() bytes */
+    int bwd_chunks;         /* chunks of the causal split backward (1: not split), with
+                               a workspace of fa_bwd_workspace_size() bytes; without
+                               the mask fa_bwd may take fewer */
     int bwd_chunk_rows;     /* rows per chunk (S when not split) */
 } fa_plan;
 

@@ -722,7 +722,7 @@ def test_rising_scores_wide_tile():
                                              (2, 1, 2000, 96, True), (1, 1, 257, 128, True),
                                              (3, 1, 520, 64, True), (1, 1, 8192, 64, True),
                                              (1, 8, 4096, 64, True), (1, 8, 4096, 16, True),
-                                             (1, 32, 2048, 16, False)])
+                                             (1, 32, 2048, 16, False), (1, 8, 4096, 64, False)])
 def test_split_backward(B, H, S, D, causal):
     """bf16 problems with few key tiles per CU: the backward runs each pass in
     chunks side by side and sums the fp32 partials (a fixed order, so still
