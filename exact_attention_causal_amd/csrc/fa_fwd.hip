@@ -553,6 +553,11 @@ int fwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t max_p
                 n = causal ? 6 : 4;
             else if (tiles <= cu || (tiles <= 2 * cu && S >= 16384))
                 n = causal ? 6 : 2;
+        } else if (D >= 64 && causal && 2 * tiles <= cu && S >= 8192) {
+            // at up to CU/2 tiles 3 causal chunks beat the two-group tile
+            // by 12-28 % (B*H = 1..4, S = 8192..32768, D = 64, 80, 128);
+            // at one tile per CU, and without the mask, no count does
+            n = 3;
         }
     } else if (D == 128) {
         // fp32 D = 128, whose chunk tile has 128 queries (fwd_gen_nw): about

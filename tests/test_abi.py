@@ -138,7 +138,9 @@ def test_fwd_workspace_size(lib):
         assert fa.fa_fwd_workspace_size(B, H, S, D, fa.FA_BF16) == 6 * B * H * S * D * 4 + 6 * B * H * S * 4
     assert fa.fa_fwd_workspace_size(1, 32, 2048, 16, fa.FA_BF16) == 0    # S < 4096
     assert fa.fa_fwd_workspace_size(1, 16, 8192, 32, fa.FA_BF16) == 0    # 512 tiles, S < 16384
-    assert fa.fa_fwd_workspace_size(1, 4, 8192, 64, fa.FA_BF16) == 0     # D = 64: two key groups instead
+    assert fa.fa_fwd_workspace_size(1, 4, 8192, 64, fa.FA_BF16) == 3 * 4 * 8192 * 64 * 4 + 3 * 4 * 8192 * 4  # CU/2
+    assert fa.fa_fwd_workspace_size(1, 8, 8192, 64, fa.FA_BF16) == 0     # D = 64, 256 tiles: two key groups
+    assert fa.fa_fwd_workspace_size(1, 8, 4096, 128, fa.FA_BF16) == 0    # CU/2 tiles, S < 8192
     # fp32, 32 tiles: ceil(256/32) = 8 chunks; 64 tiles at S >= 4096: 16; 256 tiles: 2
     assert fa.fa_fwd_workspace_size(1, 1, 8192, 64, fa.FA_F32) == 8 * 8192 * 64 * 4 + 8 * 8192 * 4
     assert fa.fa_fwd_workspace_size(1, 4, 4096, 64, fa.FA_F32) == 16 * 4 * 4096 * 64 * 4 + 16 * 4 * 4096 * 4

@@ -407,6 +407,7 @@ def _fwd_ws(q, k, v, causal, ws_bytes=None):
     (1, 5, 16400, 32, "bf16", 0),   # D <= 32 non-causal, ragged, 325 tiles, S >= 16384: 2 chunks
     (1, 10, 5000, 16, "bf16", 1),   # D <= 32, ragged, 200 tiles: 6 chunks
     (1, 12, 5000, 32, "f32", 1),    # fp32 D <= 32, ragged, 240 tiles: 8 chunks
+    (1, 2, 16300, 80, "bf16", 1),   # D >= 64, ragged, 128 tiles (CU/2): 3 chunks
 ])
 def test_fwd_ws_split_matches_oracle(B, H, S, D, dtype, causal):
     code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
