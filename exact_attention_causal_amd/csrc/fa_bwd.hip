@@ -1276,8 +1276,9 @@ BwdSplit bwd_split(int dtype, int BH, int S, int D, int causal, int ncu, size_t 
             // many per chunk.  Over B*H = 1..32, S = 1024..16384 against every
             // count up to the rule below: 8 chunks up to an eighth workgroup per
             // CU, 4 up to a quarter, 3 up to half, 2 up to two; 3-39 % faster
-            // where it differs.)
-            n = 8 * t <= cu ? 8 : 4 * t <= cu ? 4 : 2 * t <= cu ? 3 : t <= 2 * cu ? 2 : 1;
+            // where it differs.  Without the mask 2 up to half (3 were 31 %
+            // slower) and none past it (2: 1 % slower).)
+            n = 8 * t <= cu ? 8 : 4 * t <= cu ? 4 : 2 * t <= cu ? (causal ? 3 : 2) : (causal && t <= 2 * cu) ? 2 : 1;
         else
             n = (4 * t <= cu || 32 * t <= S) ? 8 : 2 * t <= cu ? 4 : t <= 2 * cu ? 2 : 1;
         // S <= 256 (one or two tiles per head; bf16 does not split there):
