@@ -83,9 +83,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * Bytes of device workspace fa_fwd_ws can use for these sizes: 0 when it runs
  * as fa_fwd; otherwise n*B*H*S*(D+1) fp32 partial values (two regions, each
  * rounded up to 256 bytes; at most 256 MiB), for problems with few query
- * tiles per compute unit, whose longest causal tile would walk every key
- * alone (the size is that of causal = 1, which splits most; a non-causal call
- * may take fewer chunks).  The compute-unit count is the current device's (256, that of one
+ * tiles per compute unit, whose longest tiles would walk many keys alone
+ * (the size is that of causal = 1, which splits most; a non-causal call may
+ * take fewer chunks).  The compute-unit count is the current device's (256, that of one
  * MI355X, when no device is visible).  Returns 0 for invalid sizes too.
  */
 size_t fa_fwd_workspace_size(int B, int H, int S, int D, int dtype);
