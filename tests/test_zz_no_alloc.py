@@ -27,17 +27,17 @@ def rel(a, b):
     return float(np.max(np.abs(a - b))) / max(float(np.max(np.abs(b))), 1e-300)
 
 
-def run(B, H, S, D, dtype, seed, with_oracle):
-    print(f"[no-alloc] B={B} H={H} S={S} D={D} dtype={dtype} seed={seed}", flush=True)
+def run(B, H, S, D, dtype, seed, with_oracle, causal=True):
+    print(f"[no-alloc] B={B} H={H} S={S} D={D} dtype={dtype} seed={seed} causal={causal}", flush=True)
     dev = torch.device("cuda:0")
     code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
     scale = 1.0 / np.sqrt(D)
     q, k, v, do = make_inputs(B, H, S, D, dtype, seed=seed)
     qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
-    o, lse = fa.forward(qd, kd, vd, causal=True)
-    dq_r, dk_r, dv_r, delta = fa.backward(qd, kd, vd, o, lse, dod, causal=True)
+    o, lse = fa.forward(qd, kd, vd, causal=causal)
+    dq_r, dk_r, dv_r, delta = fa.backward(qd, kd, vd, o, lse, dod, causal=causal)
     dq, dk, dv = (torch.full_like(qd, float("nan")) for _ in range(3))
-    rc = fa.fa_bwd_noalloc(qd, kd, vd, dod, lse, delta, dq, dk, dv, B, H, S, D, scale, 1, code)
+    rc = fa.fa_bwd_noalloc(qd, kd, vd, dod, lse, delta, dq, dk, dv, B, H, S, D, scale, int(causal), code)
     assert rc == fa.FA_OK, fa.fa_strerror(rc)
     torch.cuda.synchronize()
 
@@ -56,7 +56,7 @@ def run(B, H, S, D, dtype, seed, with_oracle):
             assert rel(g, r) <= TOL[dtype]["grad"], (n, rel(g, r))
     print(f"[no-alloc] chunks {plan.bwd_chunks}, same split: {same_split}", flush=True)
     if with_oracle:
-        ref = oracle.backward(*(x.double().numpy() for x in (q, k, v, do)), causal=True)
+        ref = oracle.backward(*(x.double().numpy() for x in (q, k, v, do)), causal=causal)
         for n, got in (("dq", dq), ("dk", dk), ("dv", dv)):
             e = rel(got.double().cpu().numpy(), ref[n])
             assert e <= TOL[dtype]["grad"], (n, e)
@@ -75,3 +75,10 @@ def test_noalloc_with_fewer_chunks_than_fa_bwd():
     # one head of 65536: a full workspace holds 2 chunks of partials (200 MB), the scratch none
     run(1, 1, 65536, 128, "bf16", seed=705, with_oracle=False)
     run(1, 3, 4096, 80, "bf16", seed=706, with_oracle=True)
+
+
+def test_noalloc_non_causal():
+    # without the mask (the split takes it into account): bf16 at CU/2 tiles (2 chunks, where the
+    # causal plan asks for 3), then a smaller fp32 problem (4 chunks of 64 rows)
+    run(1, 8, 4096, 64, "bf16", seed=707, with_oracle=True, causal=False)
+    run(1, 2, 200, 80, "f32", seed=708, with_oracle=True, causal=False)
