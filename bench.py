@@ -92,7 +92,7 @@ def parse():
                     help="only time forward and forward+backward (bf16, causal) on a list of common "
                          "training shapes, print a markdown table and exit")
     ap.add_argument("--peak", action="store_true",
-                    help="only run the matrix-core microbenchmark (libfa_peak.so): bf16 32x32x16 and "
+                    help="only run the matrix-core microbenchmark (libfa_peak.so): bf16 32x32x16, 16x16x32 and "
                          "fp32 32x32x2 MFMA loops with no memory traffic, on zero, constant and "
                          "random operands; print one JSON line per case and exit")
     ap.add_argument("--graph", action="store_true",
@@ -618,7 +618,8 @@ def peak(dev):
     # (launches of 4-19 ms; 16384 bf16 workgroups keep the last round of waves short)
     out = torch.empty(16384 * 256, device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream()
-    for name, code, blocks, iters in (("bf16", 1, 16384, 1024), ("fp32", 0, 4096, 512)):
+    forms = {0: "32x32x2", 1: "32x32x16", 2: "16x16x32"}
+    for name, code, blocks, iters in (("bf16", 1, 16384, 1024), ("bf16", 2, 16384, 2048), ("fp32", 0, 4096, 512)):
         for mode, operands in enumerate(("zeros", "constant", "random N(0,1)")):
             launch = lambda: lib.fa_peak_mfma(code, mode, blocks, iters, out.data_ptr(), stream.cuda_stream)
             for _ in range(5):
@@ -631,7 +632,7 @@ def peak(dev):
             torch.cuda.synchronize()
             ms = a.elapsed_time(b) / 10
             tf = lib.fa_peak_mfma_flop(code, blocks, iters) / (ms * 1e-3) / 1e12
-            print(json.dumps({"peak": f"mfma {name} " + ("32x32x16" if code == 1 else "32x32x2"),
+            print(json.dumps({"peak": f"mfma {name} {forms[code]}",
                               "operands": operands, "blocks": blocks, "iters": iters, "ms": round(ms, 4),
                               "tflops": round(tf, 1),
                               "published": PUBLISHED_PEAK[name], "frac": round(tf / PUBLISHED_PEAK[name], 4)}),

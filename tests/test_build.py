@@ -56,10 +56,12 @@ def test_peak_library_rejects_bad_arguments():
     lib.fa_peak_mfma_flop.argtypes = [ctypes.c_int] * 3
     lib.fa_peak_mfma_flop.restype = ctypes.c_double
     out = 0x100000
-    for dtype, mode, blocks, iters, ptr in [(2, 0, 1, 1, out), (1, 3, 1, 1, out), (1, 0, 0, 1, out),
+    for dtype, mode, blocks, iters, ptr in [(3, 0, 1, 1, out), (-1, 0, 1, 1, out), (1, 3, 1, 1, out), (1, 0, 0, 1, out),
                                             (1, 0, 1, 0, out), (0, 0, 1, 1, None), (1, 0, (1 << 22) + 1, 1, out)]:
         assert lib.fa_peak_mfma(dtype, mode, blocks, iters, ptr, None) == -1
-    # 4 waves x 16 instructions per round: 32768 FLOP each (bf16 32x32x16), 4096 (fp32 32x32x2)
+    # 4 waves x 16 instructions per round: 32768 FLOP each (bf16 32x32x16), 16384 (bf16
+    # 16x16x32), 4096 (fp32 32x32x2)
     assert lib.fa_peak_mfma_flop(1, 3, 5) == 3 * 4 * 5 * 16 * 32768
+    assert lib.fa_peak_mfma_flop(2, 3, 5) == 3 * 4 * 5 * 16 * 16384
     assert lib.fa_peak_mfma_flop(0, 3, 5) == 3 * 4 * 5 * 16 * 4096
-    assert lib.fa_peak_mfma_flop(2, 3, 5) == 0
+    assert lib.fa_peak_mfma_flop(3, 3, 5) == 0
