@@ -105,6 +105,14 @@ def _ptr(x):
     return x.data_ptr()
 
 
+def _on_stream(stream):
+    """Context making the stream of a stream argument (a torch stream or a raw HIP
+    handle; None: the current stream) current for torch's allocations and copies."""
+    if stream is None or isinstance(stream, torch.cuda.Stream):
+        return torch.cuda.stream(stream)
+    return torch.cuda.stream(torch.cuda.ExternalStream(int(stream)))
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -256,23 +264,26 @@ def forward(q, k, v, causal=True, scale=None, out=None, lse=None, workspace=None
     if workspace is not None and workspace is not False:
         ws_bytes = _workspace(workspace, q.device)
     _on_gpu(q)
-    q, k, v = (x.contiguous() for x in (q, k, v))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, S), device=q.device, dtype=torch.float32)
-    if workspace is False:
-        _check(fa_fwd(q, k, v, out, lse, B, H, S, D, scale, causal, code, stream), "fa_fwd")
+    # temporaries, contiguous copies and outputs are allocated on the stream the
+    # kernels run on, so the caching allocator never reuses them early
+    with _on_stream(stream):
+        q, k, v = (x.contiguous() for x in (q, k, v))
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, S), device=q.device, dtype=torch.float32)
+        if workspace is False:
+            _check(fa_fwd(q, k, v, out, lse, B, H, S, D, scale, causal, code, stream), "fa_fwd")
+            return out, lse
+        if workspace is None:
+            ws_bytes = fa_fwd_workspace_size(B, H, S, D, code)
+            if ws_bytes > 0:
+                workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+        _check(fa_fwd_ws(q, k, v, out, lse, workspace, ws_bytes, B, H, S, D, scale, causal, code, stream),
+               "fa_fwd_ws")
         return out, lse
-    if workspace is None:
-        ws_bytes = fa_fwd_workspace_size(B, H, S, D, code)
-        if ws_bytes > 0:
-            workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
-    _check(fa_fwd_ws(q, k, v, out, lse, workspace, ws_bytes, B, H, S, D, scale, causal, code, stream),
-           "fa_fwd_ws")
-    return out, lse
 
 
 def backward(q, k, v, o, lse, dout, causal=True, scale=None, delta=None, grads=None,
@@ -298,23 +309,26 @@ def backward(q, k, v, o, lse, dout, causal=True, scale=None, delta=None, grads=N
     if workspace is not None:
         ws_bytes = _workspace(workspace, q.device)
     _on_gpu(q)
-    q, k, v, o, dout, lse = (x.contiguous() for x in (q, k, v, o, dout, lse))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if delta is None:
-        delta = torch.empty((B, H, S), device=q.device, dtype=torch.float32)
-    if grads is None:
-        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    dq, dk, dv = grads
-    _check(fa_bwd_preprocess(o, dout, delta, B, H, S, D, code, stream), "fa_bwd_preprocess")
-    if workspace is None:
-        ws_bytes = fa_bwd_workspace_size(B, H, S, D, code)
-        if ws_bytes:
-            workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
-    # (a caller's smaller workspace disables the split backward)
-    _check(fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, ws_bytes, B, H, S, D, scale,
-                  causal, code, stream), "fa_bwd")
-    return dq, dk, dv, delta
+    # temporaries, contiguous copies and outputs are allocated on the stream the
+    # kernels run on, so the caching allocator never reuses them early
+    with _on_stream(stream):
+        q, k, v, o, dout, lse = (x.contiguous() for x in (q, k, v, o, dout, lse))
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        if delta is None:
+            delta = torch.empty((B, H, S), device=q.device, dtype=torch.float32)
+        if grads is None:
+            grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        dq, dk, dv = grads
+        _check(fa_bwd_preprocess(o, dout, delta, B, H, S, D, code, stream), "fa_bwd_preprocess")
+        if workspace is None:
+            ws_bytes = fa_bwd_workspace_size(B, H, S, D, code)
+            if ws_bytes:
+                workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+        # (a caller's smaller workspace disables the split backward)
+        _check(fa_bwd(q, k, v, dout, lse, delta, dq, dk, dv, workspace, ws_bytes, B, H, S, D, scale,
+                      causal, code, stream), "fa_bwd")
+        return dq, dk, dv, delta
 
 
 def split_chunk(Sk, n_split):
@@ -343,14 +357,17 @@ def forward_partial(q, k, v, causal=True, scale=None, q_offset=0, n_split=1, str
     code = dtype_code(q.dtype)
     Sk = _keys(q, k, v)
     _on_gpu(q)
-    q, k, v = (x.contiguous() for x in (q, k, v))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    o_parts = torch.empty((n_split, B, H, Sq, D), device=q.device, dtype=torch.float32)
-    lse_parts = torch.empty((n_split, B, H, Sq), device=q.device, dtype=torch.float32)
-    _check(fa_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Sq, Sk, D, scale, causal, q_offset,
-                          n_split, code, stream), "fa_fwd_partial")
-    return o_parts, lse_parts
+    # temporaries, contiguous copies and outputs are allocated on the stream the
+    # kernels run on, so the caching allocator never reuses them early
+    with _on_stream(stream):
+        q, k, v = (x.contiguous() for x in (q, k, v))
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        o_parts = torch.empty((n_split, B, H, Sq, D), device=q.device, dtype=torch.float32)
+        lse_parts = torch.empty((n_split, B, H, Sq), device=q.device, dtype=torch.float32)
+        _check(fa_fwd_partial(q, k, v, o_parts, lse_parts, B, H, Sq, Sk, D, scale, causal, q_offset,
+                              n_split, code, stream), "fa_fwd_partial")
+        return o_parts, lse_parts
 
 
 def merge(o_parts, lse_parts, dtype=torch.bfloat16, stream=None):
@@ -362,11 +379,14 @@ def merge(o_parts, lse_parts, dtype=torch.bfloat16, stream=None):
     _like("o_parts", o_parts, o_parts.shape, torch.float32, o_parts.device)
     _like("lse_parts", lse_parts, (n, B, H, S), torch.float32, o_parts.device)
     _on_gpu(o_parts)
-    o_parts, lse_parts = o_parts.contiguous(), lse_parts.contiguous()
-    o = torch.empty((B, H, S, D), device=o_parts.device, dtype=dtype)
-    lse = torch.empty((B, H, S), device=o_parts.device, dtype=torch.float32)
-    _check(fa_merge(o_parts, lse_parts, n, o, lse, B, H, S, D, code, stream), "fa_merge")
-    return o, lse
+    # temporaries, contiguous copies and outputs are allocated on the stream the
+    # kernels run on, so the caching allocator never reuses them early
+    with _on_stream(stream):
+        o_parts, lse_parts = o_parts.contiguous(), lse_parts.contiguous()
+        o = torch.empty((B, H, S, D), device=o_parts.device, dtype=dtype)
+        lse = torch.empty((B, H, S), device=o_parts.device, dtype=torch.float32)
+        _check(fa_merge(o_parts, lse_parts, n, o, lse, B, H, S, D, code, stream), "fa_merge")
+        return o, lse
 
 
 def forward_split_kv(q, k, v, n_split, causal=True, scale=None, stream=None):
@@ -396,18 +416,21 @@ def backward_partial(q, k, v, dout, lse, delta, causal=True, scale=None, q_offse
         for n, x, shp in zip(("dq", "dk", "dv"), grads, ((B, H, Sq, D), (B, H, Sk, D), (B, H, Sk, D))):
             _like(n, x, shp, torch.float32, q.device, contiguous=True)
     _on_gpu(q)
-    q, k, v, dout = (x.contiguous() for x in (q, k, v, dout))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if grads is None:
-        f32 = dict(device=q.device, dtype=torch.float32)
-        grads = (torch.empty((B, H, Sq, D), **f32), torch.empty((B, H, Sk, D), **f32),
-                 torch.empty((B, H, Sk, D), **f32))
-    dq, dk, dv = grads
-    _check(fa_bwd_partial(q, k, v, dout, lse.contiguous(), delta.contiguous(), dq, dk, dv,
-                          accumulate, B, H, Sq, Sk, D, scale, causal, q_offset,
-                          code, stream), "fa_bwd_partial")
-    return dq, dk, dv
+    # temporaries, contiguous copies and outputs are allocated on the stream the
+    # kernels run on, so the caching allocator never reuses them early
+    with _on_stream(stream):
+        q, k, v, dout = (x.contiguous() for x in (q, k, v, dout))
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        if grads is None:
+            f32 = dict(device=q.device, dtype=torch.float32)
+            grads = (torch.empty((B, H, Sq, D), **f32), torch.empty((B, H, Sk, D), **f32),
+                     torch.empty((B, H, Sk, D), **f32))
+        dq, dk, dv = grads
+        _check(fa_bwd_partial(q, k, v, dout, lse.contiguous(), delta.contiguous(), dq, dk, dv,
+                              accumulate, B, H, Sq, Sk, D, scale, causal, q_offset,
+                              code, stream), "fa_bwd_partial")
+        return dq, dk, dv
 
 
 # ------------------------------------------------------------- autograd ---

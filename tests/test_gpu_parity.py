@@ -796,6 +796,35 @@ def test_forward_on_a_side_stream():
     assert torch.equal(o, ref)
 
 
+@pytest.mark.parametrize("raw_handle", [False, True])
+def test_helpers_on_a_stream_that_is_not_current(raw_handle):
+    # forward/backward given a stream other than the current one: their workspaces
+    # (a split forward and a split backward at one head), copies and outputs are
+    # allocated on that stream; results equal the current-stream ones bit for bit
+    B, H, S, D = 1, 1, 8192, 128
+    assert fa.fa_fwd_workspace_size(B, H, S, D, fa.FA_BF16) > 0
+    assert fa.fa_bwd_workspace_size(B, H, S, D, fa.FA_BF16) > 4 * B * H * S
+    print(f"[parity] helpers on a side stream, raw handle={raw_handle}", flush=True)
+    q, k, v, do = make_inputs(B, H, S, D, "bf16", seed=15)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    ref_o, ref_l = fa.forward(qd, kd, vd)
+    ref_g = fa.backward(qd, kd, vd, ref_o, ref_l, dod)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    st = s.cuda_stream if raw_handle else s
+    s.wait_stream(torch.cuda.current_stream())
+    o, lse = fa.forward(qd, kd, vd, stream=st)
+    g = fa.backward(qd, kd, vd, o, lse, dod, stream=st)
+    # the current stream allocates and writes while the side stream may still run
+    junk = [torch.full((1 << 22,), float(i), device=dev) for i in range(8)]
+    s.synchronize()
+    del junk
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+    for a, b in zip(g, ref_g):
+        assert torch.equal(a, b)
+
+
 # ------------------------------------------- workgroup order of the forward ---
 
 def _banded_forward(B, H, S, heads, rows=None, causal=True, banded=True):
